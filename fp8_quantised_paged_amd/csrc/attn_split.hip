@@ -1,0 +1,431 @@
+// Split-context paged attention over an E4M3 cache for up to 32 query rows per
+// (sequence, kv-head): decode (1 query token, the GQA group as rows) and MTP
+// verify (a few query tokens with a causal mask among them).
+//
+// Work decomposition: one workgroup per (split, kv-head, sequence); its W
+// wavefronts take interleaved 64-key tiles of the split and merge their
+// online-softmax states through LDS at the end.
+//
+// Per 64-key tile a wavefront computes S^T = K Q^T and O^T += V^T P^T with
+// v_mfma_f32_16x16x32_f16:
+//  * QK: A = 16 keys x 32 dims of K (decoded from E4M3 in registers), B = the
+//    same 32 dims x 16 query rows of Q (registers for the whole kernel). Lane
+//    group g (lanes 16g..16g+15) supplies dims [g*D/4, (g+1)*D/4) of its key
+//    row across the D/32 MFMAs, so one lane reads D/4 contiguous bytes of a K
+//    row. The key of MFMA row m in M-tile t is 16*(m/4) + 4t + m%4, which puts
+//    keys 16g + 4t + i of every query row in lane group g's accumulators.
+//  * PV: A = 16 dims x 32 keys of V^T, B = the 32 keys x 16 rows of P taken
+//    straight from the QK accumulators (no cross-lane movement). Lane group g
+//    needs keys 16g .. 16g+15 of one dimension: 16 contiguous bytes of the
+//    dimension-major V page.
+// Scores are scaled once per tile by k_scale * sm_scale * log2(e); v_scale is
+// applied once to the merged accumulator.
+#include "kvfp8_internal.h"
+
+namespace kvfp8 {
+namespace {
+
+constexpr int kTile = 64;
+
+template <int D>
+struct KRegs {
+  static constexpr int kDwords = D / 16;  // D/4 bytes per lane and M-tile
+};
+
+template <int D, int P>
+struct TileRegs {
+  uint32_t k[4][D / 16];   // 4 M-tiles x D/4 bytes of one key row
+  uint32_t v[D / 16][4];   // D/16 dim blocks x 16 key bytes of one dimension
+};
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int D, int P>
+__device__ __forceinline__ void load_tile(TileRegs<D, P>& r, int t0, int end, int L, int n, int g,
+                                          const int32_t* __restrict__ btrow,
+                                          const uint8_t* __restrict__ kbase,
+                                          const uint8_t* __restrict__ vbase, int64_t page_stride) {
+  constexpr int KD = D / 16;  // dwords of K per lane and M-tile
+  // ---- K: this lane's key row in M-tile t is t0 + 16*(n/4) + 4t + n%4
+  const int krow0 = t0 + 16 * (n >> 2) + (n & 3);
+  if constexpr (P >= 16) {
+    const bool any = krow0 < end;
+    int64_t pg = any ? (int64_t)btrow[krow0 / P] : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = krow0 + 4 * t;
+      if (tok < end) {
+        const uint8_t* p = kbase + pg * page_stride + (int64_t)(tok % P) * D + g * (D / 4);
+#pragma unroll
+        for (int j = 0; j < KD / 4; ++j) {
+          u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * j);
+          r.k[t][4 * j + 0] = w[0];
+          r.k[t][4 * j + 1] = w[1];
+          r.k[t][4 * j + 2] = w[2];
+          r.k[t][4 * j + 3] = w[3];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KD; ++j) r.k[t][j] = 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = krow0 + 4 * t;
+      if (tok < end) {
+        int64_t pg = btrow[tok / P];
+        const uint8_t* p = kbase + pg * page_stride + (int64_t)(tok % P) * D + g * (D / 4);
+#pragma unroll
+        for (int j = 0; j < KD / 4; ++j) {
+          u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * j);
+          r.k[t][4 * j + 0] = w[0];
+          r.k[t][4 * j + 1] = w[1];
+          r.k[t][4 * j + 2] = w[2];
+          r.k[t][4 * j + 3] = w[3];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KD; ++j) r.k[t][j] = 0u;
+      }
+    }
+  }
+  // ---- V: keys t0 + 16g .. +15 of dimensions 16*blk + n
+  const int tv = t0 + 16 * g;
+  if constexpr (P >= 16) {
+    if (tv < L) {
+      const int64_t pg = btrow[tv / P];
+      const uint8_t* p = vbase + pg * page_stride + (int64_t)n * P + (tv % P);
+#pragma unroll
+      for (int blk = 0; blk < D / 16; ++blk) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(p + (int64_t)blk * 16 * P);
+        r.v[blk][0] = w[0];
+        r.v[blk][1] = w[1];
+        r.v[blk][2] = w[2];
+        r.v[blk][3] = w[3];
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < D / 16; ++blk) r.v[blk][0] = r.v[blk][1] = r.v[blk][2] = r.v[blk][3] = 0u;
+    }
+  } else {
+    constexpr int PIECES = 16 / P;  // pages covered by 16 keys
+    constexpr int PD = P / 4;       // dwords per piece
+#pragma unroll
+    for (int pc = 0; pc < PIECES; ++pc) {
+      const int tp = tv + pc * P;
+      if (tp < L) {
+        const int64_t pg = btrow[tp / P];
+        const uint8_t* p = vbase + pg * page_stride + (int64_t)n * P;
+#pragma unroll
+        for (int blk = 0; blk < D / 16; ++blk) {
+          const uint8_t* q = p + (int64_t)blk * 16 * P;
+          if constexpr (PD == 2) {
+            u32x2 w = *reinterpret_cast<const u32x2*>(q);
+            r.v[blk][pc * 2 + 0] = w[0];
+            r.v[blk][pc * 2 + 1] = w[1];
+          } else {
+            r.v[blk][pc] = *reinterpret_cast<const uint32_t*>(q);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < D / 16; ++blk)
+#pragma unroll
+          for (int j = 0; j < PD; ++j) r.v[blk][pc * PD + j] = 0u;
+      }
+    }
+  }
+}
+
+template <int D, int P, int NB>
+__device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, int g,
+                                             const f16x8 (&qb)[NB][D / 32], const int (&lim)[NB],
+                                             float score_scale, float (&m_run)[NB],
+                                             float (&l_run)[NB], f32x4 (&o)[NB][D / 16]) {
+  constexpr int NC = D / 32;
+  constexpr int NBLK = D / 16;
+  // keys at or past the end of the sequence may hold poison codes: zero their
+  // V bytes so that a zero probability cannot meet a NaN in the PV product
+  if (t0 + kTile > L) {
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const int c = L - (t0 + 16 * g + 4 * w4);
+      const uint32_t mask = c >= 4 ? 0xFFFFFFFFu : (c <= 0 ? 0u : ((1u << (8 * c)) - 1u));
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) r.v[blk][w4] &= mask;
+    }
+  }
+  // ---- S^T = K Q^T
+  f32x4 sc[4][NB];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      f16x8 ka = e4m3x8_to_f16(r.k[t][2 * c], r.k[t][2 * c + 1]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[nb][c], sc[t][nb], 0, 0, 0);
+    }
+  }
+  // ---- online softmax (log2 units); rows are lane columns
+  f16x8 pk[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float x[4][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * g + 4 * t + i;
+        const float v = tok < lim[nb] ? sc[t][nb][i] * score_scale : -INFINITY;
+        x[t][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = wave_max_groups(tmax);
+    const float m_new = fmaxf(m_run[nb], tmax);
+    const bool none = (m_new == -INFINITY);
+    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+    const float mref = none ? 0.0f : m_new;
+    m_run[nb] = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 2 * u + (j >> 2);
+        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(x[t][j & 3] - mref);
+        pk[nb][u][j] = p;
+        lsum += (float)p;
+      }
+    }
+    l_run[nb] = l_run[nb] * alpha + lsum;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+  }
+  // ---- O^T += V^T P^T
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f16x8 va = e4m3x8_to_f16(r.v[blk][2 * u], r.v[blk][2 * u + 1]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pk[nb][u], o[nb][blk], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int P, int NB, int W>
+__global__ __launch_bounds__(64 * W) void attn_split_kernel(const AttnArgs a) {
+  constexpr int NC = D / 32;
+  constexpr int NBLK = D / 16;
+  constexpr int ROWS = NB * 16;
+  constexpr int OPAD = D + 4;
+  __shared__ float sm_m[W][ROWS];
+  __shared__ float sm_l[W][ROWS];
+  __shared__ __attribute__((aligned(16))) float sm_o[W][ROWS][OPAD];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+
+  const int L = a.seq_lens[b];
+  int q0, T;
+  if (a.cu_q_lens != nullptr) {
+    q0 = a.cu_q_lens[b];
+    T = a.cu_q_lens[b + 1] - q0;
+  } else {
+    q0 = b;
+    T = 1;
+  }
+  T = min(T, a.max_q_len);
+  const int G = a.group;
+  const int nrows = T * G;
+  const int S = a.num_splits;
+  const int chunk = ((L + kTile * S - 1) / (kTile * S)) * kTile;
+  const int start = s * chunk;
+  const int end = min(start + chunk, L);
+  const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
+
+  // ---- Q operand (dims g*D/4 + 8c + i of row n of each 16-row block)
+  f16x8 qb[NB][NC];
+  int lim[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int rr = nb * 16 + n;
+    if (rr < nrows) {
+      const int i = rr / G;
+      const int h = kvh * G + rr % G;
+      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + g * (D / 4);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 8 * c);
+      lim[nb] = min(end, L - T + i + 1);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qb[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      lim[nb] = 0;
+    }
+  }
+
+  float m_run[NB], l_run[NB];
+  f32x4 o[NB][NBLK];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t page_stride = (int64_t)a.n_kv_heads * P * D;
+  const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;
+  const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
+  const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
+
+  // ---- tiles: ping-pong register buffers, next tile's loads in flight while
+  // the current one is computed
+  int it = wave;
+  if (it < ntiles) {
+    TileRegs<D, P> ra, rb;
+    load_tile<D, P>(ra, start + it * kTile, end, L, n, g, btrow, kbase, vbase, page_stride);
+    while (true) {
+      int nx = it + W;
+      if (nx < ntiles)
+        load_tile<D, P>(rb, start + nx * kTile, end, L, n, g, btrow, kbase, vbase, page_stride);
+      compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+      it = nx;
+      if (it >= ntiles) break;
+      nx = it + W;
+      if (nx < ntiles)
+        load_tile<D, P>(ra, start + nx * kTile, end, L, n, g, btrow, kbase, vbase, page_stride);
+      compute_tile<D, P, NB>(rb, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+      it = nx;
+      if (it >= ntiles) break;
+    }
+  }
+
+  // ---- merge the wavefronts' states through LDS
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lrow = wave_sum_groups(l_run[nb]);
+    const int rr = nb * 16 + n;
+    if (g == 0) {
+      sm_m[wave][rr] = m_run[nb];
+      sm_l[wave][rr] = lrow;
+    }
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+      *reinterpret_cast<f32x4*>(&sm_o[wave][rr][16 * blk + 4 * g]) = o[nb][blk];
+  }
+  __syncthreads();
+
+  constexpr int DG8 = D / 8;
+  const bool direct = (a.out != nullptr);
+  for (int item = threadIdx.x; item < ROWS * DG8; item += 64 * W) {
+    const int rr = item / DG8;
+    const int dg = item % DG8;
+    if (rr >= nrows) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][rr]);
+    const float ref = (M == -INFINITY) ? 0.0f : M;
+    float lsum = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = sm_m[w][rr];
+      const float wt = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - ref);
+      lsum += wt * sm_l[w][rr];
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sm_o[w][rr][8 * dg]);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(&sm_o[w][rr][8 * dg + 4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] += wt * x0[j];
+        acc[4 + j] += wt * x1[j];
+      }
+    }
+    const int i = rr / G;
+    const int h = kvh * G + rr % G;
+    const int64_t qrow = q0 + i;
+    if (direct) {
+      const float f = lsum > 0.0f ? a.v_scale / lsum : 0.0f;
+      uint32_t pk4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 lo = (_Float16)(acc[2 * j] * f);
+        const _Float16 hi = (_Float16)(acc[2 * j + 1] * f);
+        pk4[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *reinterpret_cast<u32x4*>(a.out + (qrow * a.n_q_heads + h) * D + 8 * dg) =
+          u32x4{pk4[0], pk4[1], pk4[2], pk4[3]};
+    } else {
+      const int64_t unit = (qrow * a.n_q_heads + h) * S + s;
+      float* dst = a.ws_o + unit * D + 8 * dg;
+      *reinterpret_cast<f32x4*>(dst) =
+          f32x4{acc[0] * a.v_scale, acc[1] * a.v_scale, acc[2] * a.v_scale, acc[3] * a.v_scale};
+      *reinterpret_cast<f32x4*>(dst + 4) =
+          f32x4{acc[4] * a.v_scale, acc[5] * a.v_scale, acc[6] * a.v_scale, acc[7] * a.v_scale};
+      if (dg == 0) {
+        a.ws_m[unit] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+        a.ws_l[unit] = lsum;
+      }
+    }
+  }
+}
+
+template <int D, int P, int NB>
+hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
+  constexpr int W = 4;
+  dim3 grid((unsigned)a.num_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);
+  attn_split_kernel<D, P, NB, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, int P>
+hipError_t launch2(const AttnArgs& a, int rows, hipStream_t stream) {
+  if (rows <= 16) return launch3<D, P, 1>(a, stream);
+  return launch3<D, P, 2>(a, stream);
+}
+
+template <int D>
+hipError_t launch1(const AttnArgs& a, int rows, hipStream_t stream) {
+  switch (a.page_size) {
+    case 4: return launch2<D, 4>(a, rows, stream);
+    case 8: return launch2<D, 8>(a, rows, stream);
+    case 16: return launch2<D, 16>(a, rows, stream);
+    case 32: return launch2<D, 32>(a, rows, stream);
+    case 64: return launch2<D, 64>(a, rows, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_split(const AttnArgs& a, int rows_per_kvh, hipStream_t stream) {
+  if (a.head_dim == 128) return launch1<128>(a, rows_per_kvh, stream);
+  if (a.head_dim == 64) return launch1<64>(a, rows_per_kvh, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvfp8

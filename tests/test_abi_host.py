@@ -1,0 +1,205 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches a kernel).
+
+Every invalid-argument case is rejected by the library's host validation
+before any HIP call, so these run without a GPU. Fake device pointers are
+only ever passed together with an argument that is rejected.
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp8_quantised_paged_amd import kvfp8
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvfp8.h")
+L = kvfp8.raw()
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+MIS = 0x10001
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("kv_quant_write", "kv_calibrate_amax", "paged_attn_e4m3_decode", "paged_attn_e4m3_verify",
+              "split_reduce_fp32"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(kvfp8.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvfp8.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    # nothing else of ours leaks out
+    ours = {s for s in exported if s.startswith(("kv", "paged", "split", "_ZN5kvfp8"))}
+    assert ours == set(names)
+
+
+def test_status_strings():
+    assert kvfp8.status_str(0) == "KVFP8_OK"
+    assert kvfp8.status_str(2) == "KVFP8_BAD_SCALE"
+    assert kvfp8.status_str(6) == "KVFP8_HIP_ERROR"
+    assert kvfp8.status_str(99) == "KVFP8_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes():
+    assert kvfp8.kvfp8_attn_workspace_bytes(32, 32, 128, 4) == 32 * 32 * 4 * 130 * 4
+    assert kvfp8.kvfp8_attn_workspace_bytes(4, 32, 128, 64) == 4 * 32 * 64 * 130 * 4
+    assert kvfp8.kvfp8_attn_workspace_bytes(0, 32, 128, 4) == 0
+    assert kvfp8.kvfp8_attn_workspace_bytes(3, 8, 64, -1) == 0
+
+
+def write(**kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, n=4, hkv=4, d=128, p=16, pages=10, ks=1.0, vs=1.0, kc=FAKE, vc=FAKE)
+    a.update(kw)
+    return L.kv_quant_write(a["k"], a["v"], a["slots"], a["n"], a["hkv"], a["d"], a["p"], a["pages"],
+                            a["ks"], a["vs"], a["kc"], a["vc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), kvfp8.INVALID_ARG),
+    (dict(hkv=0), kvfp8.INVALID_ARG),
+    (dict(d=96), kvfp8.UNSUPPORTED),
+    (dict(p=12), kvfp8.UNSUPPORTED),
+    (dict(p=128), kvfp8.UNSUPPORTED),
+    (dict(ks=float("nan")), kvfp8.BAD_SCALE),
+    (dict(ks=float("inf")), kvfp8.BAD_SCALE),
+    (dict(vs=0.0), kvfp8.BAD_SCALE),
+    (dict(vs=-0.5), kvfp8.BAD_SCALE),
+    (dict(ks=1e-40), kvfp8.BAD_SCALE),
+    (dict(k=None), kvfp8.INVALID_ARG),
+    (dict(slots=None), kvfp8.INVALID_ARG),
+    (dict(vc=None), kvfp8.INVALID_ARG),
+    (dict(k=MIS), kvfp8.INVALID_ARG),
+    (dict(kc=MIS), kvfp8.INVALID_ARG),
+])
+def test_quant_write_rejects(kw, status):
+    assert write(**kw) == status
+    assert kvfp8.last_error()
+
+
+def test_quant_write_zero_tokens_is_a_noop():
+    assert write(n=0, k=None, v=None) == kvfp8.OK
+    # but the scale gate still applies: no unit-scale fallback, even for an empty write
+    assert write(n=0, ks=0.0) == kvfp8.BAD_SCALE
+
+
+def decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=32, hkv=4, d=128, p=16, mp=8, ks=0.1,
+             vs=0.1, sm=0.088, s=1, ws=None, wsb=0, out=FAKE)
+    a.update(kw)
+    return L.paged_attn_e4m3_decode(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["b"], a["hq"], a["hkv"],
+                                    a["d"], a["p"], a["mp"], a["ks"], a["vs"], a["sm"], a["s"], a["ws"],
+                                    a["wsb"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), kvfp8.INVALID_ARG),
+    (dict(bt=None), kvfp8.INVALID_ARG),
+    (dict(sl=None), kvfp8.INVALID_ARG),
+    (dict(b=-1), kvfp8.INVALID_ARG),
+    (dict(hq=30), kvfp8.INVALID_ARG),
+    (dict(hkv=0), kvfp8.INVALID_ARG),
+    (dict(mp=0), kvfp8.INVALID_ARG),
+    (dict(d=80), kvfp8.UNSUPPORTED),
+    (dict(p=128), kvfp8.UNSUPPORTED),
+    (dict(s=0), kvfp8.UNSUPPORTED),
+    (dict(s=257), kvfp8.UNSUPPORTED),
+    (dict(hq=64, hkv=1), kvfp8.UNSUPPORTED),
+    (dict(ks=float("nan")), kvfp8.BAD_SCALE),
+    (dict(vs=0.0), kvfp8.BAD_SCALE),
+    (dict(sm=-1.0), kvfp8.BAD_SCALE),
+    (dict(sm=float("inf")), kvfp8.BAD_SCALE),
+    (dict(q=MIS), kvfp8.INVALID_ARG),
+    (dict(vc=MIS), kvfp8.INVALID_ARG),
+    (dict(out=MIS), kvfp8.INVALID_ARG),
+    (dict(out=None), kvfp8.INVALID_ARG),
+    (dict(s=4), kvfp8.WORKSPACE),
+    (dict(s=4, ws=FAKE, wsb=1024), kvfp8.WORKSPACE),
+    (dict(s=4, ws=MIS, wsb=1 << 30), kvfp8.INVALID_ARG),
+])
+def test_decode_rejects(kw, status):
+    assert decode(**kw) == status
+
+
+def test_decode_empty_batch_is_a_noop():
+    assert decode(b=0) == kvfp8.OK
+
+
+def verify(**kw):
+    a = dict(q=FAKE, cu=FAKE, tq=8, mq=4, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=32, hkv=4, d=128,
+             p=16, mp=8, ks=0.1, vs=0.1, sm=0.088, s=1, ws=None, wsb=0, out=FAKE)
+    a.update(kw)
+    return L.paged_attn_e4m3_verify(a["q"], a["cu"], a["tq"], a["mq"], a["kc"], a["vc"], a["bt"], a["sl"],
+                                    a["b"], a["hq"], a["hkv"], a["d"], a["p"], a["mp"], a["ks"], a["vs"],
+                                    a["sm"], a["s"], a["ws"], a["wsb"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), kvfp8.INVALID_ARG),
+    (dict(tq=-1), kvfp8.INVALID_ARG),
+    (dict(mq=0), kvfp8.INVALID_ARG),
+    (dict(ks=0.0), kvfp8.BAD_SCALE),
+    (dict(d=256), kvfp8.UNSUPPORTED),
+    (dict(s=2), kvfp8.WORKSPACE),
+    # a long chunk (64 query tokens x 8 heads) goes to the chunk kernel, which takes no splits
+    (dict(mq=64, tq=128, s=2, ws=FAKE, wsb=1 << 30), kvfp8.UNSUPPORTED),
+])
+def test_verify_rejects(kw, status):
+    assert verify(**kw) == status
+
+
+def reduce(**kw):
+    a = dict(o=FAKE, m=FAKE, l=FAKE, r=4, hq=32, d=128, s=8, out=FAKE, lse=None)
+    a.update(kw)
+    return L.split_reduce_fp32(a["o"], a["m"], a["l"], a["r"], a["hq"], a["d"], a["s"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=-1), kvfp8.INVALID_ARG),
+    (dict(hq=0), kvfp8.INVALID_ARG),
+    (dict(d=32), kvfp8.UNSUPPORTED),
+    (dict(s=0), kvfp8.UNSUPPORTED),
+    (dict(s=300), kvfp8.UNSUPPORTED),
+    (dict(o=None), kvfp8.INVALID_ARG),
+    (dict(out=None), kvfp8.INVALID_ARG),
+    (dict(o=FAKE + 4), kvfp8.INVALID_ARG),
+])
+def test_split_reduce_rejects(kw, status):
+    assert reduce(**kw) == status
+
+
+def test_split_reduce_zero_rows_is_a_noop():
+    assert reduce(r=0, o=None) == kvfp8.OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, -1, 8, FAKE, FAKE), kvfp8.INVALID_ARG),
+    ((FAKE, 2, -8, FAKE, FAKE), kvfp8.INVALID_ARG),
+    ((FAKE, 2, 8, None, FAKE), kvfp8.INVALID_ARG),
+    ((FAKE, 2, 8, FAKE, None), kvfp8.INVALID_ARG),
+    ((None, 2, 8, FAKE, FAKE), kvfp8.INVALID_ARG),
+    ((MIS, 2, 8, FAKE, FAKE), kvfp8.INVALID_ARG),
+    ((FAKE, 0, 8, FAKE, FAKE), kvfp8.OK),
+])
+def test_calibrate_rejects(args, status):
+    assert L.kv_calibrate_amax(*args, None) == status
+
+
+def test_codec_helpers_reject():
+    assert L.kvfp8_e4m3_encode_f32(FAKE, FAKE, -1, None) == kvfp8.INVALID_ARG
+    assert L.kvfp8_e4m3_decode_f32(None, FAKE, 5, None) == kvfp8.INVALID_ARG
+    assert L.kvfp8_e4m3_decode_f32(FAKE, FAKE, 0, None) == kvfp8.OK

@@ -1,0 +1,341 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bit-exact for E4M3 codes, cache bytes, amax and scales; attention within
+|gpu - ref| <= 2e-3 + 1e-2 |ref| elementwise (fp16 output, fp32 accumulation).
+Every input is a seeded synthetic draw from synth/.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (calibrate_amax, e4m3_decode, e4m3_encode, paged_attention, split_partials,
+                    split_reduce)
+from synth import make_batch, make_config
+from tests.gpu_common import (DeviceBatch, assert_close_attn, dev, oracle_caches, oracle_scales,
+                              report)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    from fp8_quantised_paged_amd import kvfp8
+    assert torch.cuda.is_available()
+    return kvfp8
+
+
+def sm_of(bt):
+    return np.float32(1.0 / np.sqrt(bt.head_dim))
+
+
+# ----------------------------------------------------------------- codec
+
+def test_device_decode_all_codes(K):
+    codes = np.arange(256, dtype=np.uint8)
+    got = K.kvfp8_e4m3_decode_f32(dev(codes)).cpu().numpy().astype(np.float64)
+    ref = e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+def test_device_encode_boundaries_and_random(K):
+    vals = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    parts = [mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf)),
+             vals.astype(np.float32),
+             np.array([448, 449, 463.9, 464, 464.1, 480, 500, 1e6, np.inf, 0.0, 2 ** -10, 3 * 2 ** -10,
+                       2 ** -11, 1e-30, 1e-45], np.float32)]
+    rng = np.random.default_rng(0)
+    parts.append((rng.standard_normal(500_000) * np.exp2(rng.integers(-14, 12, 500_000))).astype(np.float32))
+    x = np.concatenate(parts + [-p for p in parts])
+    got = K.kvfp8_e4m3_encode_f32(dev(x)).cpu().numpy()
+    assert np.array_equal(got, e4m3_encode(x))
+    nan = np.array([np.nan, -np.nan], np.float32)
+    assert np.array_equal(K.kvfp8_e4m3_encode_f32(dev(nan)).cpu().numpy(), e4m3_encode(nan))
+
+
+# ----------------------------------------------------------------- calibration
+
+@pytest.mark.parametrize("which", ["tiny_same_tensors", "decode_calib_set", "ragged_len"])
+def test_calibrate_bit_exact(K, which):
+    if which == "tiny_same_tensors":
+        bt = make_config(1)
+        x = np.stack([bt.k.reshape(-1), bt.v.reshape(-1)])
+    elif which == "decode_calib_set":
+        bt = make_config(2, seq_len_override=64)
+        x = np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])
+    else:
+        rng = np.random.default_rng(3)
+        x = (rng.standard_normal((7, 1001)) * 3).astype(np.float16)  # rows not 16-byte multiples
+    amax, scale, st = K.kv_calibrate_amax(dev(x))
+    ra, rs, rst = calibrate_amax(x)
+    assert st == rst == 0
+    assert np.array_equal(amax.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_calibrate_mixed_workload_48_tensors(K):
+    from synth.workloads import make_mixed_calibration
+    x = make_mixed_calibration()
+    amax, scale, st = K.kv_calibrate_amax(dev(x))
+    ra, rs, rst = calibrate_amax(x)
+    assert st == rst == 0 and x.shape[0] == 48
+    assert np.array_equal(amax.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_calibrate_error_statuses(K):
+    x = np.zeros((3, 64), dtype=np.float16)
+    x[0] = 1.5
+    x[2, 7] = np.inf
+    amax, scale, st = K.kv_calibrate_amax(dev(x), check=False)
+    ra, rs, rst = calibrate_amax(x)
+    assert st == rst == K.NONFINITE_INPUT
+    assert np.array_equal(amax.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    x[2, 7] = 0
+    amax, scale, st = K.kv_calibrate_amax(dev(x), check=False)
+    assert st == K.BAD_SCALE and calibrate_amax(x)[2] == K.BAD_SCALE
+    assert amax.cpu().numpy()[1] == 0 and scale.cpu().numpy()[1] == 0
+
+
+# ----------------------------------------------------------------- write
+
+def _gpu_write(K, db, ks, vs):
+    K.kv_quant_write(db.k, db.v, db.slots, float(ks), float(vs), db.k_cache, db.v_cache)
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged_p16_d128", "p8_d64", "p32", "p64"])
+def test_quant_write_bit_exact(K, case):
+    bt = {
+        "tiny": lambda: make_config(1),
+        "ragged_p16_d128": lambda: make_batch([1, 17, 300, 64], [1, 1, 4, 2], 32, 4, 128, 16, seed=41),
+        "p8_d64": lambda: make_batch([33, 70], [1, 3], 8, 2, 64, 8, seed=42),
+        "p32": lambda: make_batch([100, 31, 64], [1, 1, 1], 16, 2, 128, 32, seed=43),
+        "p64": lambda: make_batch([200, 5], [1, 1], 32, 4, 128, 64, seed=44),
+    }[case]()
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    assert np.array_equal(db.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy(), vc)
+
+
+def test_quant_write_skips_padding_and_saturates(K):
+    bt = make_batch([40], [1], 8, 2, 64, 16, seed=45)
+    bt.k[7, 0, :8] = np.float16(60000.0)  # far beyond 448 * scale: saturates
+    bt.k[5, 1, :4] = np.float16(-0.0)
+    slots = bt.slot_mapping.copy()
+    slots[::3] = -1
+    slots[1] = bt.num_pages * bt.page_size + 5  # past the cache: skipped
+    db = DeviceBatch(bt)
+    db.slots = dev(slots)
+    K.kv_quant_write(db.k, db.v, db.slots, 0.01, 0.02, db.k_cache, db.v_cache)
+    from oracle import new_caches, quant_write
+    kc, vc = new_caches(bt.num_pages, bt.n_kv_heads, bt.page_size, bt.head_dim)
+    quant_write(bt.k, bt.v, slots, np.float32(0.01), np.float32(0.02), kc, vc)
+    assert np.array_equal(db.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy(), vc)
+    assert (kc == 0x7E).any()
+
+
+# ----------------------------------------------------------------- attention
+
+def _run_decode(K, db, ks, vs, sm, S):
+    bt = db.bt
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
+    if ws is not None:
+        ws.fill_(float("nan"))  # every partial the reduce reads must have been written
+    return K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens,
+                                    float(ks), float(vs), float(sm), num_splits=S, workspace=ws)
+
+
+def _run_verify(K, db, ks, vs, sm, S):
+    bt = db.bt
+    ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
+    if ws is not None:
+        ws.fill_(float("nan"))
+    return K.paged_attn_e4m3_verify(db.q, db.cu_q, int(bt.q_lens.max()), db.k_cache, db.v_cache,
+                                    db.block_table, db.seq_lens, float(ks), float(vs), float(sm),
+                                    num_splits=S, workspace=ws)
+
+
+DECODE_CASES = {
+    "tiny": lambda: make_config(1),
+    "d128_p16_ragged": lambda: make_batch([1, 63, 64, 65, 1000, 333], [1] * 6, 32, 4, 128, 16, seed=51),
+    "d64_p8": lambda: make_batch([5, 130, 77], [1] * 3, 16, 4, 64, 8, seed=52),
+    "d128_p64_g4": lambda: make_batch([700, 64, 129], [1] * 3, 16, 4, 128, 64, seed=53),
+    "d128_p32_g16": lambda: make_batch([300, 41], [1] * 2, 32, 2, 128, 32, seed=54),
+    "d64_p4_g32": lambda: make_batch([90, 17], [1] * 2, 32, 1, 64, 4, seed=55),
+}
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 8])
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_parity(K, case, S):
+    bt = DECODE_CASES[case]()
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = sm_of(bt)
+    out = _run_decode(K, db, sc[0], sc[1], sm, S).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"{case} S={S}")
+
+
+VERIFY_CASES = {
+    "mtp3_small": lambda: make_batch([1024, 70, 4, 300], [4] * 4, 32, 4, 128, 16, seed=61),
+    "ragged_q": lambda: make_batch([50, 9, 200, 3], [1, 2, 4, 3], 32, 4, 128, 16, seed=62),
+    "d64_p4": lambda: make_batch([100, 257], [4, 2], 8, 2, 64, 4, seed=63),
+    "g4_q8": lambda: make_batch([129, 64], [8, 5], 16, 4, 64, 16, seed=64),
+}
+
+
+@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("case", list(VERIFY_CASES))
+def test_verify_parity(K, case, S):
+    bt = VERIFY_CASES[case]()
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = sm_of(bt)
+    out = _run_verify(K, db, sc[0], sc[1], sm, S).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"{case} S={S}")
+
+
+def test_partials_match_oracle_partials(K):
+    bt = make_batch([1000, 257, 64, 3], [1, 1, 1, 1], 32, 4, 128, 16, seed=71)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    S = 4
+    sm = sm_of(bt)
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
+    ws.fill_(float("nan"))
+    K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, float(sc[0]),
+                             float(sc[1]), float(sm), num_splits=S, workspace=ws, partials_only=True)
+    o, m, l = [t.cpu().numpy().astype(np.float64) for t in K.workspace_views(ws, bt.batch, bt.n_q_heads,
+                                                                             bt.head_dim, S)]
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    ro, rm, rl = split_partials(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm,
+                                S, granule=64)
+    assert np.array_equal(np.isneginf(m), np.isneginf(rm))
+    fin = np.isfinite(rm)
+    np.testing.assert_allclose(m[fin], rm[fin], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(l, rl, rtol=2e-3, atol=1e-5)
+    scale = np.maximum(rl[..., None], 1.0)
+    assert (np.abs(o - ro) <= 2e-3 * scale + 1e-2 * np.abs(ro)).all()
+
+
+def test_split_reduce_of_oracle_partials(K):
+    bt = make_batch([500, 64, 130], [1, 1, 1], 32, 4, 128, 16, seed=72)
+    _, sc = oracle_scales(bt)
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    S = 7
+    ro, rm, rl = split_partials(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1],
+                                sm_of(bt), S, granule=64)
+    o32, m32, l32 = ro.astype(np.float32), rm.astype(np.float32), rl.astype(np.float32)
+    ref, ref_lse = split_reduce(o32, m32, l32)
+    out, lse = K.split_reduce_fp32(dev(o32), dev(m32), dev(l32), with_lse=True)
+    assert_close_attn(out.cpu().numpy(), ref, "reduce")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+
+
+def test_split_reduce_all_empty_rows(K):
+    o = np.zeros((2, 4, 5, 64), np.float32)
+    m = np.full((2, 4, 5), -np.inf, np.float32)
+    l = np.zeros((2, 4, 5), np.float32)
+    m[1, 2, 3], l[1, 2, 3], o[1, 2, 3] = 1.0, 2.0, 4.0
+    out, lse = K.split_reduce_fp32(dev(o), dev(m), dev(l), with_lse=True)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+    assert (out[1, 2] == 2.0).all() and abs(lse[1, 2] - (1 + np.log(2))) < 1e-5
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_single_token_context_returns_v_for_every_code(K):
+    """With one key, the output is v_scale * decode(v): run every non-NaN code
+    through the V path (v_scale = 1 so the output is exact in fp16)."""
+    bt = make_batch([1, 1], [1, 1], 4, 2, 64, 16, seed=81)
+    db = DeviceBatch(bt)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0x00, 0x80], np.uint8)
+    codes = codes.reshape(2, 2, 64)  # [sequence, kv-head, dim]
+    vc = db.v_cache.cpu().numpy()
+    kc = db.k_cache.cpu().numpy()
+    for b in range(2):
+        page = bt.block_table[b, 0]
+        vc[page, :, :, 0] = codes[b]
+        kc[page, :, 0, :] = 0x38
+    db.v_cache.copy_(dev(vc))
+    db.k_cache.copy_(dev(kc))
+    out = K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, 1.0, 1.0,
+                                   0.125).cpu().numpy()
+    ref = e4m3_decode(codes)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(out[b, h].astype(np.float64), ref[b, h // 2])
+
+
+def test_page_permutation_bit_identical(K):
+    bt = make_batch([300, 77], [1, 1], 32, 4, 128, 16, seed=82)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    out1 = _run_decode(K, db, sc[0], sc[1], sm_of(bt), 2).cpu().numpy()
+    relabel = np.random.default_rng(1).permutation(bt.num_pages)
+    kc2 = torch.empty_like(db.k_cache)
+    vc2 = torch.empty_like(db.v_cache)
+    kc2[dev(relabel)] = db.k_cache
+    vc2[dev(relabel)] = db.v_cache
+    db.k_cache, db.v_cache = kc2, vc2
+    db.block_table = dev(np.where(bt.block_table >= 0, relabel[np.maximum(bt.block_table, 0)], -1)
+                         .astype(np.int32))
+    out2 = _run_decode(K, db, sc[0], sc[1], sm_of(bt), 2).cpu().numpy()
+    assert np.array_equal(out1.view(np.uint16), out2.view(np.uint16))
+
+
+def test_gqa_identical_queries_bit_identical_and_deterministic(K):
+    bt = make_batch([500], [1], 32, 4, 128, 16, seed=83)
+    bt.q[0, 1] = bt.q[0, 0]
+    bt.q[0, 7] = bt.q[0, 0]
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    a = _run_decode(K, db, sc[0], sc[1], sm_of(bt), 3).cpu().numpy()
+    b = _run_decode(K, db, sc[0], sc[1], sm_of(bt), 3).cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(a[0, 0].view(np.uint16), a[0, 1].view(np.uint16))
+    assert np.array_equal(a[0, 0].view(np.uint16), a[0, 7].view(np.uint16))
+
+
+def test_verify_row_equals_decode_of_shorter_sequence(K):
+    bt = make_batch([200], [4], 32, 4, 128, 16, seed=84)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = sm_of(bt)
+    ver = _run_verify(K, db, sc[0], sc[1], sm, 1).cpu().numpy()
+    for i in range(4):
+        dec = K.paged_attn_e4m3_decode(db.q[i:i + 1].contiguous(), db.k_cache, db.v_cache, db.block_table,
+                                       dev(np.array([200 - 4 + i + 1], np.int32)), float(sc[0]),
+                                       float(sc[1]), float(sm)).cpu().numpy()
+        err, _ = report(ver[i], dec[0].astype(np.float64))
+        assert err <= 2e-3
+
+
+def test_power_of_two_v_scale_equivariance(K):
+    bt = make_batch([123, 64], [1, 1], 32, 4, 128, 16, seed=85)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    a = _run_decode(K, db, sc[0], sc[1], sm_of(bt), 1).cpu().numpy()
+    b = _run_decode(K, db, sc[0], np.float32(sc[1] * 2), sm_of(bt), 1).cpu().numpy()
+    assert np.array_equal(b, a * np.float16(2))
