@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark over a calibrated E4M3 paged KV cache (one MI355X).
+
+One step is one layer's decode hot path over the batch: quantise-write the new
+token of every sequence into the E4M3 cache, split-context attention over the
+whole context, and the FP32 split reduce. The headline workload is batch 32 at
+a 4,096-token context (32 query / 4 KV heads, head_dim 128, page 16); the 32k
+(batch 32, context 32,768) and 256k (batch 4, context 262,144, page 64, 64
+splits, outlier channels) points are reported beside it.
+
+Timing: the caches are rotated over enough copies that every step reads its KV
+from HBM (the 256 MB Infinity Cache cannot hold them). Each point's steps are
+captured in HIP graphs and the timed region replays exactly --steps of them,
+bracketed by device synchronisation and HIP events. The attention kernel's own
+average duration comes from a graph of back-to-back attention launches timed
+with HIP events on the stream the kernels run on.
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+METRIC = "decode attention KV GB/s & % of HBM peak; tokens/s per layer at 4k/32k/256k"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(seq_lens, n_q_heads, n_kv_heads, head_dim, max_pages):
+    """Bytes one decode step must move at minimum: every cached K and V byte,
+    Q in, O out (fp16), the block table and the sequence lengths."""
+    B = len(seq_lens)
+    kv = int(np.sum(seq_lens, dtype=np.int64)) * n_kv_heads * head_dim * 2
+    qo = 2 * B * n_q_heads * head_dim * 2
+    meta = B * max_pages * 4 + B * 4
+    return kv, kv + qo + meta
+
+
+class Point:
+    """One decode workload resident on the GPU with `nsets` cache copies."""
+
+    def __init__(self, K, torch, name, layout, k_src, v_src, calib, num_splits, nsets):
+        self.K, self.torch, self.name, self.bt = K, torch, name, layout
+        bt = layout
+        dev = "cuda"
+        self.S = num_splits
+        self.B, self.Hq, self.Hkv, self.D, self.P = bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.page_size
+        amax, scale, _ = K.kv_calibrate_amax(calib)
+        self.ks, self.vs = float(scale[0].item()), float(scale[1].item())
+        self.sm = float(np.float32(1.0 / np.sqrt(self.D)))
+        self.q = torch.from_numpy(bt.q).to(dev)
+        self.block_table = torch.from_numpy(bt.block_table).to(dev)
+        self.seq_lens = torch.from_numpy(bt.seq_lens).to(dev)
+        slots = torch.from_numpy(bt.slot_mapping).to(dev)
+        new_rows = torch.from_numpy(bt.new_token_rows()).to(dev)
+        self.k_new = k_src[new_rows].contiguous()
+        self.v_new = v_src[new_rows].contiguous()
+        self.slots_new = slots[new_rows].contiguous()
+        self.sets = []
+        for _ in range(nsets):
+            kc = torch.full((bt.num_pages, self.Hkv, self.P, self.D), 0x7F, dtype=torch.uint8, device=dev)
+            vc = torch.full((bt.num_pages, self.Hkv, self.D, self.P), 0x7F, dtype=torch.uint8, device=dev)
+            K.kv_quant_write(k_src, v_src, slots, self.ks, self.vs, kc, vc)
+            self.sets.append((kc, vc))
+        self.ws = K.workspace(self.B, self.Hq, self.D, self.S)
+        self.ws_o, self.ws_m, self.ws_l = K.workspace_views(self.ws, self.B, self.Hq, self.D, self.S)
+        self.out = torch.empty_like(self.q)
+        self.kv_bytes, self.alg_bytes = algorithmic_bytes(bt.seq_lens, self.Hq, self.Hkv, self.D,
+                                                          bt.max_pages)
+        torch.cuda.synchronize()
+
+    def attend(self, i):
+        kc, vc = self.sets[i % len(self.sets)]
+        self.K.paged_attn_e4m3_decode(self.q, kc, vc, self.block_table, self.seq_lens, self.ks, self.vs,
+                                      self.sm, num_splits=self.S, workspace=self.ws, partials_only=True)
+
+    def step(self, i):
+        kc, vc = self.sets[i % len(self.sets)]
+        self.K.kv_quant_write(self.k_new, self.v_new, self.slots_new, self.ks, self.vs, kc, vc)
+        self.attend(i)
+        self.K.split_reduce_fp32(self.ws_o, self.ws_m, self.ws_l, out=self.out)
+
+    def capture(self, fn, count):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)  # warm the launch path outside the capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(count):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return g
+
+    def time_steps(self, steps, warmup):
+        """Exactly `steps` graph-replayed steps; returns (seconds per step, out)."""
+        torch = self.torch
+        n = len(self.sets)
+        full = self.capture(self.step, n)
+        singles = [self.capture(lambda i, j=j: self.step(j), 1) for j in range(n)]
+        for w in range(warmup):
+            singles[w % n].replay()
+        torch.cuda.synchronize()
+        # the graphs must reproduce the eager result exactly
+        self.step(0)
+        torch.cuda.synchronize()
+        eager = self.out.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        done = 0
+        while done + n <= steps:
+            full.replay()
+            done += n
+        while done < steps:
+            singles[done % n].replay()
+            done += 1
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu = e0.elapsed_time(e1) / 1e3
+        singles[0].replay()
+        torch.cuda.synchronize()
+        replay_matches = bool(torch.equal(self.out, eager))
+        return max(gpu, 0.0) / steps, wall / steps, replay_matches
+
+    def time_attention_kernel(self, launches):
+        """Average attention-kernel duration from HIP events around a graph of
+        back-to-back attention launches on the capture stream."""
+        torch = self.torch
+        g = self.capture(self.attend, launches)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / launches
+
+
+def default_splits(batch, n_kv_heads, seq_len, cus=256):
+    """Enough workgroups to cover the CUs about twice, with splits of at least
+    512 keys."""
+    units = batch * n_kv_heads
+    s = max(1, -(-2 * cus // units))
+    s = min(s, max(1, seq_len // 512), 256)
+    return s
+
+
+def cpu_baseline(seconds_target=10.0):
+    """The fp64 oracle timed on host cores over sampled sequences of the 4k
+    decode workload (same seeded inputs as the GPU run)."""
+    from oracle import calibrate_amax, new_caches, paged_attention, quant_write
+    from synth import make_config
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    bt = make_config(2)
+    _, sc, _ = calibrate_amax(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)]))
+    sample = [0, 1, 2, 3]
+    kc, vc = new_caches(bt.num_pages, bt.n_kv_heads, bt.page_size, bt.head_dim)
+    for b in sample:
+        s0, s1 = int(bt.cu_seq_lens[b]), int(bt.cu_seq_lens[b + 1])
+        quant_write(bt.k[s0:s1], bt.v[s0:s1], bt.slot_mapping[s0:s1], sc[0], sc[1], kc, vc)
+    sm = np.float32(1.0 / np.sqrt(bt.head_dim))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm,
+                        rows=sample)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target:
+            break
+    kv_bytes = reps * len(sample) * 4096 * bt.n_kv_heads * bt.head_dim * 2
+    return {
+        "value": kv_bytes / el / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle attention over {len(sample)} of the 32 sequences of the 4k decode "
+                  f"workload, repeated {reps}x ({el:.1f} s); host os.cpu_count()={os.cpu_count()}",
+        "tokens_per_s_per_layer": reps * len(sample) / el,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--points", default="4k,32k,256k")
+    ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-launches", type=int, default=60)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp8_quantised_paged_amd import kvfp8 as K
+    from synth import make_config
+    from synth.device import normal_kv
+
+    torch.cuda.set_device(0)
+    points = [p for p in args.points.split(",") if p]
+    results = {}
+
+    for p in points:
+        log(f"setting up point {p}")
+        if p == "4k":
+            bt = make_config(2)
+            k_src = torch.from_numpy(bt.k).cuda()
+            v_src = torch.from_numpy(bt.v).cuda()
+            calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
+            S = args.splits or default_splits(bt.batch, bt.n_kv_heads, 4096)
+            nsets, steps = 6, args.steps
+        elif p == "32k":
+            bt = make_config(2, seq_len_override=32768, values=False)
+            total = int(bt.cu_seq_lens[-1])
+            k_src = normal_kv(total, 4, 128, bt.seed * 10 + 1)
+            v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2)
+            cal = normal_kv(2 * 2048, 4, 128, bt.seed * 10 + 3)
+            calib = cal.view(2, -1)
+            S = default_splits(bt.batch, bt.n_kv_heads, 32768)
+            nsets, steps = 2, max(10, args.steps // 3)
+        elif p == "256k":
+            bt = make_config(4, values=False)
+            total = int(bt.cu_seq_lens[-1])
+            k_src = normal_kv(total, 4, 128, bt.seed * 10 + 1, bt.outlier_channels_k)
+            v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2, bt.outlier_channels_v)
+            ck = normal_kv(2048, 4, 128, bt.seed * 10 + 3, bt.outlier_channels_k)
+            cv = normal_kv(2048, 4, 128, bt.seed * 10 + 4, bt.outlier_channels_v)
+            calib = torch.stack([ck.reshape(-1), cv.reshape(-1)])
+            S = 64
+            nsets, steps = 2, max(10, args.steps // 3)
+        else:
+            raise SystemExit(f"unknown point {p}")
+        pt = Point(K, torch, p, bt, k_src, v_src, calib, S, nsets)
+        del k_src, v_src
+        torch.cuda.empty_cache()
+        log(f"{p}: batch {pt.B} splits {S} kv bytes {pt.kv_bytes}; timing {steps} steps")
+        sec, wall, same = pt.time_steps(steps, args.warmup)
+        launches = args.kernel_launches if p == "4k" else max(6, args.kernel_launches // 6)
+        launches = max(launches // nsets, 1) * nsets
+        kern = pt.time_attention_kernel(launches)
+        results[p] = {
+            "batch": pt.B, "seq_len": int(bt.seq_lens[0]), "num_splits": S, "page_size": pt.P,
+            "steps": steps, "ms_per_step": sec * 1e3, "host_ms_per_step": wall * 1e3,
+            "kv_bytes_per_step": pt.kv_bytes, "algorithmic_bytes_per_step": pt.alg_bytes,
+            "kv_gbs": pt.kv_bytes / sec / 1e9, "tokens_per_s_per_layer": pt.B / sec,
+            "attn_kernel_us": kern * 1e6, "attn_kernel_gbs": pt.alg_bytes / kern / 1e9,
+            "graph_replay_matches_eager": same, "cache_sets": nsets,
+        }
+        log(f"{p}: {json.dumps(results[p])}")
+        del pt
+        torch.cuda.empty_cache()
+
+    main = results.get("4k") or results[points[0]]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        cpu = cpu_baseline()
+    achieved = main["attn_kernel_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": main["kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": main["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": main["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode_b32_ctx4096_h32kv4_d128_p16_e4m3", "batch": main["batch"],
+                   "seq_len": main["seq_len"], "n_q_heads": 32, "n_kv_heads": 4, "head_dim": 128,
+                   "page_size": main["page_size"], "num_splits": main["num_splits"],
+                   "kv_cache": "e4m3 (OCP), per-layer K/V scales", "accumulate": "f32"},
+        "pct_hbm_peak": 100.0 * main["kv_gbs"] / HBM_PEAK_GBS,
+        "tokens_per_s_per_layer": {p: r["tokens_per_s_per_layer"] for p, r in results.items()},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "attn_split_kernel<128,16,1,4>", "kernel_us": main["attn_kernel_us"]},
+        "cpu_baseline": cpu,
+        "points": results,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,10 +9,10 @@
 // Per 64-key tile a wavefront computes S^T = K Q^T and O^T += V^T P^T with
 // v_mfma_f32_16x16x32_f16:
 //  * QK: A = 16 keys x 32 dims of K (decoded from E4M3 in registers), B = the
-//    same 32 dims x 16 query rows of Q (registers for the whole kernel). Lane
-//    group g (lanes 16g..16g+15) supplies dims [g*D/4, (g+1)*D/4) of its key
-//    row across the D/32 MFMAs, so one lane reads D/4 contiguous bytes of a K
-//    row. The key of MFMA row m in M-tile t is 16*(m/4) + 4t + m%4, which puts
+//    same 32 dims x 16 query rows of Q (registers for the whole kernel). The
+//    contraction order over dims is free, so MFMA c takes, in lane group g
+//    (lanes 16g..16g+15), dims 16g + 64*(c/2) + 8*(c%2) + i: each load
+//    instruction then reads 64 contiguous bytes of 16 key rows. The key of MFMA row m in M-tile t is 16*(m/4) + 4t + m%4, which puts
 //    keys 16g + 4t + i of every query row in lane group g's accumulators.
 //  * PV: A = 16 dims x 32 keys of V^T, B = the 32 keys x 16 rows of P taken
 //    straight from the QK accumulators (no cross-lane movement). Lane group g
@@ -26,11 +26,6 @@ namespace kvfp8 {
 namespace {
 
 constexpr int kTile = 64;
-
-template <int D>
-struct KRegs {
-  static constexpr int kDwords = D / 16;  // D/4 bytes per lane and M-tile
-};
 
 template <int D, int P>
 struct TileRegs {
@@ -50,65 +45,71 @@ __device__ __forceinline__ float wave_sum_groups(float x) {
   return x;
 }
 
+// Per-lane page ids of one 64-key tile: the page of this lane's K rows (one per
+// M-tile when pages are shorter than 16 keys) and of its 16 V keys (one per
+// piece of P keys when P < 16). Indices are clamped to the sequence's last
+// page, so no entry past it is ever read.
+template <int P>
+struct PageRegs {
+  static constexpr int NK = (P >= 16) ? 1 : 4;
+  static constexpr int NV = (P >= 16) ? 1 : 16 / P;
+  int32_t k[NK];
+  int32_t v[NV];
+};
+
+// Vector loads, issued two tiles ahead of use: the in-order vector memory
+// counter then never makes a wait on these ids wait on K/V bytes that are
+// still in flight for the tile being computed.
+template <int P>
+__device__ __forceinline__ void load_pages(PageRegs<P>& pr, const int32_t* __restrict__ btrow, int t0,
+                                           int last, int n, int g) {
+  const int krel = 16 * (n >> 2) + (n & 3);
+#pragma unroll
+  for (int t = 0; t < PageRegs<P>::NK; ++t) pr.k[t] = btrow[min((t0 + krel + 4 * t) / P, last)];
+#pragma unroll
+  for (int pc = 0; pc < PageRegs<P>::NV; ++pc) pr.v[pc] = btrow[min((t0 + 16 * g + pc * P) / P, last)];
+}
+
+// K/V bytes are read exactly once per call, so they are loaded non-temporally
+// (streamed past the caches instead of evicting the block table, Q and the
+// partials).
 template <int D, int P>
-__device__ __forceinline__ void load_tile(TileRegs<D, P>& r, int t0, int end, int L, int n, int g,
-                                          const int32_t* __restrict__ btrow,
-                                          const uint8_t* __restrict__ kbase,
+__device__ __forceinline__ void load_tile(TileRegs<D, P>& r, const PageRegs<P>& pr, int t0, int end,
+                                          int L, int n, int g, const uint8_t* __restrict__ kbase,
                                           const uint8_t* __restrict__ vbase, int64_t page_stride) {
   constexpr int KD = D / 16;  // dwords of K per lane and M-tile
-  // ---- K: this lane's key row in M-tile t is t0 + 16*(n/4) + 4t + n%4
-  const int krow0 = t0 + 16 * (n >> 2) + (n & 3);
-  if constexpr (P >= 16) {
-    const bool any = krow0 < end;
-    int64_t pg = any ? (int64_t)btrow[krow0 / P] : 0;
+  // ---- K: the key row of this lane in M-tile t is t0 + 16*(n/4) + 4t + n%4.
+  // Lane group g reads dims [16g, 16g+16) (and [64+16g, 80+16g) for D = 128),
+  // so each load instruction covers 64 contiguous bytes of every key row.
+  const int krel = 16 * (n >> 2) + (n & 3);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = krow0 + 4 * t;
-      if (tok < end) {
-        const uint8_t* p = kbase + pg * page_stride + (int64_t)(tok % P) * D + g * (D / 4);
+  for (int t = 0; t < 4; ++t) {
+    const int tok = t0 + krel + 4 * t;
+    if (tok < end) {
+      const int64_t pg = pr.k[PageRegs<P>::NK == 1 ? 0 : t];
+      const uint8_t* p = kbase + pg * page_stride + (int64_t)(tok % P) * D + 16 * g;
 #pragma unroll
-        for (int j = 0; j < KD / 4; ++j) {
-          u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * j);
-          r.k[t][4 * j + 0] = w[0];
-          r.k[t][4 * j + 1] = w[1];
-          r.k[t][4 * j + 2] = w[2];
-          r.k[t][4 * j + 3] = w[3];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < KD; ++j) r.k[t][j] = 0u;
+      for (int j = 0; j < KD / 4; ++j) {
+        u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
+        r.k[t][4 * j + 0] = w[0];
+        r.k[t][4 * j + 1] = w[1];
+        r.k[t][4 * j + 2] = w[2];
+        r.k[t][4 * j + 3] = w[3];
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = krow0 + 4 * t;
-      if (tok < end) {
-        int64_t pg = btrow[tok / P];
-        const uint8_t* p = kbase + pg * page_stride + (int64_t)(tok % P) * D + g * (D / 4);
-#pragma unroll
-        for (int j = 0; j < KD / 4; ++j) {
-          u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * j);
-          r.k[t][4 * j + 0] = w[0];
-          r.k[t][4 * j + 1] = w[1];
-          r.k[t][4 * j + 2] = w[2];
-          r.k[t][4 * j + 3] = w[3];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < KD; ++j) r.k[t][j] = 0u;
-      }
+      for (int j = 0; j < KD; ++j) r.k[t][j] = 0u;
     }
   }
   // ---- V: keys t0 + 16g .. +15 of dimensions 16*blk + n
   const int tv = t0 + 16 * g;
   if constexpr (P >= 16) {
     if (tv < L) {
-      const int64_t pg = btrow[tv / P];
+      const int64_t pg = pr.v[0];
       const uint8_t* p = vbase + pg * page_stride + (int64_t)n * P + (tv % P);
 #pragma unroll
       for (int blk = 0; blk < D / 16; ++blk) {
-        u32x4 w = *reinterpret_cast<const u32x4*>(p + (int64_t)blk * 16 * P);
+        u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (int64_t)blk * 16 * P));
         r.v[blk][0] = w[0];
         r.v[blk][1] = w[1];
         r.v[blk][2] = w[2];
@@ -125,7 +126,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D, P>& r, int t0, int end, in
     for (int pc = 0; pc < PIECES; ++pc) {
       const int tp = tv + pc * P;
       if (tp < L) {
-        const int64_t pg = btrow[tp / P];
+        const int64_t pg = pr.v[pc];
         const uint8_t* p = vbase + pg * page_stride + (int64_t)n * P;
 #pragma unroll
         for (int blk = 0; blk < D / 16; ++blk) {
@@ -184,7 +185,6 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
   f16x8 pk[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    float x[4][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -192,7 +192,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * g + 4 * t + i;
         const float v = tok < lim[nb] ? sc[t][nb][i] * score_scale : -INFINITY;
-        x[t][i] = v;
+        sc[t][nb][i] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = wave_max_groups(tmax);
@@ -207,7 +207,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int t = 2 * u + (j >> 2);
-        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(x[t][j & 3] - mref);
+        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(sc[t][nb][j & 3] - mref);
         pk[nb][u][j] = p;
         lsum += (float)p;
       }
@@ -230,7 +230,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
 }
 
 template <int D, int P, int NB, int W>
-__global__ __launch_bounds__(64 * W) void attn_split_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64 * W, (NB == 1 ? 2 : 1)) void attn_split_kernel(const AttnArgs a) {
   constexpr int NC = D / 32;
   constexpr int NBLK = D / 16;
   constexpr int ROWS = NB * 16;
@@ -274,9 +274,10 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(const AttnArgs a) {
     if (rr < nrows) {
       const int i = rr / G;
       const int h = kvh * G + rr % G;
-      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + g * (D / 4);
+      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 8 * c);
+      for (int c = 0; c < NC; ++c)
+        qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
       lim[nb] = min(end, L - T + i + 1);
     } else {
 #pragma unroll
@@ -299,25 +300,29 @@ __global__ __launch_bounds__(64 * W) void attn_split_kernel(const AttnArgs a) {
   const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;
   const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
+  const int last = L > 0 ? (L - 1) / P : 0;
 
-  // ---- tiles: ping-pong register buffers, next tile's loads in flight while
-  // the current one is computed
+  // ---- tiles: two register buffers (the next tile's K/V in flight while the
+  // current one is computed) and two page-id sets (ids two tiles ahead)
   int it = wave;
   if (it < ntiles) {
     TileRegs<D, P> ra, rb;
-    load_tile<D, P>(ra, start + it * kTile, end, L, n, g, btrow, kbase, vbase, page_stride);
+    PageRegs<P> pa, pb;
+    load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+    if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+    load_tile<D, P>(ra, pa, start + it * kTile, end, L, n, g, kbase, vbase, page_stride);
     while (true) {
-      int nx = it + W;
-      if (nx < ntiles)
-        load_tile<D, P>(rb, start + nx * kTile, end, L, n, g, btrow, kbase, vbase, page_stride);
+      if (it + 2 * W < ntiles) load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
+      if (it + W < ntiles)
+        load_tile<D, P>(rb, pb, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
       compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
-      it = nx;
+      it += W;
       if (it >= ntiles) break;
-      nx = it + W;
-      if (nx < ntiles)
-        load_tile<D, P>(ra, start + nx * kTile, end, L, n, g, btrow, kbase, vbase, page_stride);
+      if (it + 2 * W < ntiles) load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
+      if (it + W < ntiles)
+        load_tile<D, P>(ra, pa, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
       compute_tile<D, P, NB>(rb, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
-      it = nx;
+      it += W;
       if (it >= ntiles) break;
     }
   }

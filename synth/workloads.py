@@ -121,6 +121,7 @@ def make_batch(
     outlier_df: float = 3.0,
     outlier_scale: float = 8.0,
     spare_pages: int = 3,
+    values: bool = True,
 ) -> PagedBatch:
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     q_lens = np.asarray(q_lens, dtype=np.int32)
@@ -155,11 +156,12 @@ def make_batch(
     out_v = sorted(rng_out.choice(n_ch, size=n_out, replace=False).tolist()) if n_out else []
 
     total = int(cu_seq[-1])
-    k = np.empty((total, n_kv_heads, head_dim), dtype=np.float16)
-    v = np.empty((total, n_kv_heads, head_dim), dtype=np.float16)
+    shape = (total, n_kv_heads, head_dim) if values else (0, n_kv_heads, head_dim)
+    k = np.empty(shape, dtype=np.float16)
+    v = np.empty(shape, dtype=np.float16)
     k_seq = s_k.spawn(B)
     v_seq = s_v.spawn(B)
-    for b in range(B):
+    for b in (range(B) if values else ()):
         rk = np.random.Generator(np.random.PCG64(k_seq[b]))
         rv = np.random.Generator(np.random.PCG64(v_seq[b]))
         L = int(seq_lens[b])
@@ -174,7 +176,7 @@ def make_batch(
     q = _normal_f16(rq, (int(cu_q[-1]), n_q_heads, head_dim))
 
     calib_k = calib_v = None
-    if calib_tokens:
+    if calib_tokens and values:
         rc = np.random.Generator(np.random.PCG64(s_cal))
         calib_k = _with_outliers(_normal_f16(rc, (calib_tokens, n_kv_heads, head_dim)),
                                  out_k, rc, outlier_df, outlier_scale)
@@ -196,28 +198,29 @@ def mtp3_context_lengths(seed: int, batch: int = 16) -> np.ndarray:
     return rng.choice(np.array([1024, 4096, 8192, 32768]), size=batch).astype(np.int32)
 
 
-def make_config(idx: int, layer: int = 0, seq_len_override: Optional[int] = None) -> PagedBatch:
+def make_config(idx: int, layer: int = 0, seq_len_override: Optional[int] = None,
+                values: bool = True) -> PagedBatch:
     """The five named workloads. For the mixed workload (5) one layer's batch is
     returned: 8 decode sequences at 8,192 followed by one sequence holding a
     2,048-token chunk over a 30,000-token prior context."""
     seed = SEED_BASE + idx
     if idx == 1:
-        return make_batch([100, 257], [1, 1], 8, 2, 64, 4, seed, name=CONFIG_NAMES[1])
+        return make_batch([100, 257], [1, 1], 8, 2, 64, 4, seed, name=CONFIG_NAMES[1], values=values)
     if idx == 2:
         L = seq_len_override or 4096
         return make_batch([L] * 32, [1] * 32, 32, 4, 128, 16, seed, name=CONFIG_NAMES[2],
-                          calib_tokens=2048)
+                          calib_tokens=2048, values=values)
     if idx == 3:
         lens = mtp3_context_lengths(seed)
         return make_batch(lens, [4] * 16, 32, 4, 128, 16, seed, name=CONFIG_NAMES[3],
-                          calib_tokens=2048)
+                          calib_tokens=2048, values=values)
     if idx == 4:
         L = seq_len_override or 262144
         return make_batch([L] * 4, [1] * 4, 32, 4, 128, 64, seed, name=CONFIG_NAMES[4],
-                          calib_tokens=2048, outlier_frac=0.02)
+                          calib_tokens=2048, outlier_frac=0.02, values=values)
     if idx == 5:
         return make_batch([8192] * 8 + [32048], [1] * 8 + [2048], 32, 4, 128, 16,
-                          seed * 100 + layer, name=f"{CONFIG_NAMES[5]}_layer{layer}")
+                          seed * 100 + layer, name=f"{CONFIG_NAMES[5]}_layer{layer}", values=values)
     raise ValueError(f"unknown config {idx}")
 
 

@@ -338,4 +338,8 @@ def test_power_of_two_v_scale_equivariance(K):
     _gpu_write(K, db, sc[0], sc[1])
     a = _run_decode(K, db, sc[0], sc[1], sm_of(bt), 1).cpu().numpy()
     b = _run_decode(K, db, sc[0], np.float32(sc[1] * 2), sm_of(bt), 1).cpu().numpy()
-    assert np.array_equal(b, a * np.float16(2))
+    # exact where the fp16 output is a normal number; an fp16 subnormal rounds at a
+    # fixed absolute step, so there doubling and rounding commute only to 2**-24
+    normal = np.abs(a) >= np.float16(2.0 ** -14)
+    assert np.array_equal(b[normal], a[normal] * np.float16(2))
+    assert (np.abs(b[~normal].astype(np.float64) - 2 * a[~normal].astype(np.float64)) <= 2.0 ** -24).all()
