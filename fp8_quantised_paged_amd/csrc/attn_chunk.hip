@@ -1,8 +1,350 @@
-// Query-tiled causal chunk attention (long q_len); see launch_attn_chunk.
+// Query-tiled causal chunk attention over an E4M3 paged cache: the prefill /
+// catch-up chunk of a mixed batch (many query tokens per sequence).
+//
+// One workgroup of W = 8 wavefronts owns R = 256 query rows (row = token * G +
+// head-in-group) of one (sequence, kv-head) and walks the keys visible to them
+// in 64-key tiles. Every tile is loaded from HBM once per workgroup, decoded
+// from E4M3 to fp16 once, and staged in LDS (K token-major, V dimension-major,
+// double-buffered so the next tile's loads overlap the current tile's math).
+// Each wavefront then computes S^T = K Q^T and O^T += V^T P^T for its 32 rows
+// with v_mfma_f32_16x16x32_f16, exactly as the split kernel does per lane (the
+// same key permutation makes the QK accumulators the PV B operand).
+//
+// XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs;
+// when the (query tile, kv-head) plane divides evenly, the linear index is
+// remapped so that each XCD serves a contiguous run of query tiles of as few
+// kv-heads as possible, and its L2 holds one head's K/V stream.
 #include "kvfp8_internal.h"
 
 namespace kvfp8 {
+namespace {
 
-hipError_t launch_attn_chunk(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kTile = 64;
+constexpr int kWaves = 8;
+constexpr int kNB = 2;                       // 16-row blocks per wavefront
+constexpr int kRows = kWaves * kNB * 16;     // 256 rows per workgroup
+constexpr int kXcds = 8;
+
+template <int D>
+struct ChunkLds {
+  static constexpr int KS = D + 8;           // fp16 row stride of K (keys x dims)
+  static constexpr int VS = kTile + 8;       // fp16 row stride of V^T (dims x keys)
+  _Float16 k[2][kTile][KS];
+  _Float16 v[2][D][VS];
+};
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Raw bytes of one tile held by one thread: 16 K bytes (16 dims of one key) and
+// 16 V bytes (16 keys of one dim).
+struct ChunkRegs {
+  u32x4 k;
+  u32x4 v;
+};
+
+template <int D, int P>
+__device__ __forceinline__ void chunk_load(ChunkRegs& r, int tid, int t0, int L,
+                                           const int32_t* __restrict__ btrow,
+                                           const uint8_t* __restrict__ kbase,
+                                           const uint8_t* __restrict__ vbase, int64_t page_stride) {
+  constexpr int KSEG = D / 16;  // 16-byte segments per key row
+  const int last = (L - 1) / P;
+  r.k = u32x4{0u, 0u, 0u, 0u};
+  r.v = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kTile * KSEG) {
+    const int kk = tid / KSEG;
+    const int seg = tid % KSEG;
+    const int tok = t0 + kk;
+    if (tok < L) {
+      const int64_t pg = btrow[min(tok / P, last)];
+      r.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          kbase + pg * page_stride + (int64_t)(tok % P) * D + 16 * seg));
+    }
+  }
+  if (tid < D * 4) {
+    const int d = tid >> 2;
+    const int kseg = tid & 3;
+    const int tv = t0 + 16 * kseg;
+    if constexpr (P >= 16) {
+      if (tv < L) {
+        const int64_t pg = btrow[min(tv / P, last)];
+        r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            vbase + pg * page_stride + (int64_t)d * P + (tv % P)));
+      }
+    } else {
+      constexpr int PIECES = 16 / P;
+#pragma unroll
+      for (int pc = 0; pc < PIECES; ++pc) {
+        const int tp = tv + pc * P;
+        if (tp < L) {
+          const int64_t pg = btrow[min(tp / P, last)];
+          const uint8_t* q = vbase + pg * page_stride + (int64_t)d * P;
+          if constexpr (P == 8) {
+            u32x2 w = *reinterpret_cast<const u32x2*>(q);
+            r.v[2 * pc] = w[0];
+            r.v[2 * pc + 1] = w[1];
+          } else {
+            r.v[pc] = *reinterpret_cast<const uint32_t*>(q);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Decode the thread's bytes to fp16 and store them in LDS buffer `buf`. Keys at
+// or past the sequence end are stored as zeros (their slots may hold poison).
+template <int D>
+__device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const ChunkRegs& r, int tid, int t0,
+                                            int L) {
+  constexpr int KSEG = D / 16;
+  if (tid < kTile * KSEG) {
+    const int kk = tid / KSEG;
+    const int seg = tid % KSEG;
+    f16x8 a = e4m3x8_to_f16(r.k[0], r.k[1]);
+    f16x8 b = e4m3x8_to_f16(r.k[2], r.k[3]);
+    *reinterpret_cast<f16x8*>(&s.k[buf][kk][16 * seg]) = a;
+    *reinterpret_cast<f16x8*>(&s.k[buf][kk][16 * seg + 8]) = b;
+  }
+  if (tid < D * 4) {
+    const int d = tid >> 2;
+    const int kseg = tid & 3;
+    u32x4 w = r.v;
+    const int c = L - (t0 + 16 * kseg);  // valid keys among the 16
+    if (c < 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cj = c - 4 * j;
+        w[j] &= cj >= 4 ? 0xFFFFFFFFu : (cj <= 0 ? 0u : ((1u << (8 * cj)) - 1u));
+      }
+    }
+    f16x8 a = e4m3x8_to_f16(w[0], w[1]);
+    f16x8 b = e4m3x8_to_f16(w[2], w[3]);
+    *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg]) = a;
+    *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg + 8]) = b;
+  }
+}
+
+template <int D, int P>
+__global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnArgs a) {
+  constexpr int NC = D / 32;
+  constexpr int NBLK = D / 16;
+  __shared__ __attribute__((aligned(16))) ChunkLds<D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int b = blockIdx.z;
+
+  // ---- XCD-aware (query tile, kv-head) assignment
+  const int nx = gridDim.x;
+  const int total = nx * a.n_kv_heads;
+  int lin = blockIdx.x + nx * blockIdx.y;
+  if (total % kXcds == 0) {
+    const int per = total / kXcds;
+    lin = (lin % kXcds) * per + lin / kXcds;
+  }
+  const int qt = lin % nx;
+  const int kvh = lin / nx;
+
+  const int L = a.seq_lens[b];
+  const int q0 = a.cu_q_lens[b];
+  const int T = min(a.cu_q_lens[b + 1] - q0, a.max_q_len);
+  const int G = a.group;
+  const int nrows = T * G;
+  const int row0 = qt * kRows;
+  if (row0 >= nrows) return;  // whole workgroup exits together
+  const int row_end = min(row0 + kRows, nrows);
+  // keys visible to the workgroup's last row
+  const int n_keys = min(L, L - T + (row_end - 1) / G + 1);
+  const int ntiles = n_keys > 0 ? (n_keys + kTile - 1) / kTile : 0;
+
+  // ---- this wavefront's 32 rows: Q operand and causal limits
+  f16x8 qb[kNB][NC];
+  int lim[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int rr = row0 + wave * (kNB * 16) + nb * 16 + n;
+    if (rr < nrows) {
+      const int i = rr / G;
+      const int h = kvh * G + rr % G;
+      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
+      lim[nb] = L - T + i + 1;
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qb[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      lim[nb] = 0;
+    }
+  }
+  // smallest limit among the wavefront's rows: tiles below it need no mask
+  int wave_lim;
+  {
+    const int first = row0 + wave * (kNB * 16);
+    wave_lim = first < nrows ? L - T + first / G + 1 : 0;
+  }
+
+  float m_run[kNB], l_run[kNB];
+  f32x4 o[kNB][NBLK];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t page_stride = (int64_t)a.n_kv_heads * P * D;
+  const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;
+  const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
+  const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
+  const int krel = 16 * (n >> 2) + (n & 3);
+
+  ChunkRegs regs;
+  if (ntiles > 0) {
+    chunk_load<D, P>(regs, tid, 0, L, btrow, kbase, vbase, page_stride);
+    chunk_store<D>(sm, 0, regs, tid, 0, L);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = it * kTile;
+    if (it + 1 < ntiles) chunk_load<D, P>(regs, tid, t0 + kTile, L, btrow, kbase, vbase, page_stride);
+
+    // ---- S^T = K Q^T from LDS
+    f32x4 sc[4][kNB];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) sc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const _Float16* krow = &sm.k[buf][krel + 4 * t][16 * g];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 64 * (c >> 1) + 8 * (c & 1));
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[nb][c], sc[t][nb], 0, 0, 0);
+      }
+    }
+    // ---- online softmax (log2 units)
+    const bool masked = (t0 + kTile > wave_lim);
+    f16x8 pk[kNB][2];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = t0 + 16 * g + 4 * t + i;
+          float v = sc[t][nb][i] * a.score_scale;
+          if (masked) v = tok < lim[nb] ? v : -INFINITY;
+          sc[t][nb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = wave_max_groups(tmax);
+      const float m_new = fmaxf(m_run[nb], tmax);
+      const bool none = (m_new == -INFINITY);
+      const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+      const float mref = none ? 0.0f : m_new;
+      m_run[nb] = m_new;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = 2 * u + (j >> 2);
+          const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(sc[t][nb][j & 3] - mref);
+          pk[nb][u][j] = p;
+          lsum += (float)p;
+        }
+      }
+      l_run[nb] = l_run[nb] * alpha + lsum;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+    }
+    // ---- O^T += V^T P^T from LDS
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f16x8 va = *reinterpret_cast<const f16x8*>(&sm.v[buf][16 * blk + n][16 * g + 8 * u]);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pk[nb][u], o[nb][blk], 0, 0, 0);
+      }
+    }
+    if (it + 1 < ntiles) chunk_store<D>(sm, buf ^ 1, regs, tid, t0 + kTile, L);
+    __syncthreads();
+  }
+
+  // ---- normalise and write fp16 rows (lane holds dims 16*blk + 4g + i of row n)
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const float lrow = wave_sum_groups(l_run[nb]);
+    const int rr = row0 + wave * (kNB * 16) + nb * 16 + n;
+    if (rr >= nrows) continue;
+    const int i = rr / G;
+    const int h = kvh * G + rr % G;
+    const float f = lrow > 0.0f ? a.v_scale / lrow : 0.0f;
+    uint16_t* dst = a.out + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 4 * g;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const _Float16 h0 = (_Float16)(o[nb][blk][0] * f);
+      const _Float16 h1 = (_Float16)(o[nb][blk][1] * f);
+      const _Float16 h2 = (_Float16)(o[nb][blk][2] * f);
+      const _Float16 h3 = (_Float16)(o[nb][blk][3] * f);
+      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+      *reinterpret_cast<u32x2*>(dst + 16 * blk) = u32x2{w0, w1};
+    }
+  }
+}
+
+template <int D, int P>
+hipError_t launch_p(const AttnArgs& a, hipStream_t stream) {
+  const int rows = a.max_q_len * a.group;
+  dim3 grid((unsigned)((rows + kRows - 1) / kRows), (unsigned)a.n_kv_heads, (unsigned)a.batch);
+  attn_chunk_kernel<D, P><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
+  switch (a.page_size) {
+    case 4: return launch_p<D, 4>(a, stream);
+    case 8: return launch_p<D, 8>(a, stream);
+    case 16: return launch_p<D, 16>(a, stream);
+    case 32: return launch_p<D, 32>(a, stream);
+    case 64: return launch_p<D, 64>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_chunk(const AttnArgs& a, hipStream_t stream) {
+  if (a.out == nullptr || a.cu_q_lens == nullptr) return hipErrorInvalidValue;
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace kvfp8

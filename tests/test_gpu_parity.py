@@ -343,3 +343,46 @@ def test_power_of_two_v_scale_equivariance(K):
     normal = np.abs(a) >= np.float16(2.0 ** -14)
     assert np.array_equal(b[normal], a[normal] * np.float16(2))
     assert (np.abs(b[~normal].astype(np.float64) - 2 * a[~normal].astype(np.float64)) <= 2.0 ** -24).all()
+
+
+# ----------------------------------------------------------------- prefill chunk (query-tiled kernel)
+
+CHUNK_CASES = {
+    "chunk_over_prior": lambda: make_batch([700], [200], 32, 4, 128, 16, seed=91),
+    "ragged_no_prior": lambda: make_batch([100, 70, 300], [50, 70, 33], 32, 4, 128, 16, seed=92),
+    "d64_p4_g4": lambda: make_batch([257, 90], [120, 90], 16, 4, 64, 4, seed=93),
+    "p64_g8": lambda: make_batch([1000, 64], [300, 20], 32, 4, 128, 64, seed=94),
+    "p8_g16": lambda: make_batch([333], [65], 32, 2, 128, 8, seed=95),
+    "mixed_layer_small": lambda: make_batch([1000] * 8 + [1256], [1] * 8 + [256], 32, 4, 128, 16, seed=96),
+}
+
+
+@pytest.mark.parametrize("case", list(CHUNK_CASES))
+def test_chunk_parity(K, case):
+    bt = CHUNK_CASES[case]()
+    assert int(bt.q_lens.max()) * (bt.n_q_heads // bt.n_kv_heads) > 32  # takes the chunk kernel
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = sm_of(bt)
+    out = _run_verify(K, db, sc[0], sc[1], sm, 1).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, case)
+
+
+def test_chunk_rows_match_split_kernel_rows(K):
+    """The same rows computed by the chunk kernel (long q) and by the split
+    kernel (one query token at a time) agree within the tolerance."""
+    bt = make_batch([400], [96], 32, 4, 128, 16, seed=97)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = sm_of(bt)
+    chunk = _run_verify(K, db, sc[0], sc[1], sm, 1).cpu().numpy()
+    for i in (0, 31, 32, 95):
+        dec = K.paged_attn_e4m3_decode(db.q[i:i + 1].contiguous(), db.k_cache, db.v_cache, db.block_table,
+                                       dev(np.array([400 - 96 + i + 1], np.int32)), float(sc[0]),
+                                       float(sc[1]), float(sm)).cpu().numpy()
+        err, _ = report(chunk[i], dec[0].astype(np.float64))
+        assert err <= 2e-3, (i, err)
