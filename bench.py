@@ -155,15 +155,6 @@ class Point:
         return e0.elapsed_time(e1) / 1e3 / launches
 
 
-def default_splits(batch, n_kv_heads, seq_len, cus=256):
-    """Enough workgroups to cover the CUs about twice, with splits of at least
-    512 keys."""
-    units = batch * n_kv_heads
-    s = max(1, -(-2 * cus // units))
-    s = min(s, max(1, seq_len // 512), 256)
-    return s
-
-
 def cpu_baseline(seconds_target=10.0):
     """The fp64 oracle timed on host cores over sampled sequences of the 4k
     decode workload (same seeded inputs as the GPU run)."""
@@ -234,7 +225,7 @@ def main():
             k_src = torch.from_numpy(bt.k).cuda()
             v_src = torch.from_numpy(bt.v).cuda()
             calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
-            S = args.splits or default_splits(bt.batch, bt.n_kv_heads, 4096)
+            S = args.splits or K.default_splits(bt.batch, bt.n_kv_heads, 4096)
             nsets, steps = 6, args.steps
         elif p == "32k":
             bt = make_config(2, seq_len_override=32768, values=False)
@@ -243,7 +234,7 @@ def main():
             v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2)
             cal = normal_kv(2 * 2048, 4, 128, bt.seed * 10 + 3)
             calib = cal.view(2, -1)
-            S = default_splits(bt.batch, bt.n_kv_heads, 32768)
+            S = K.default_splits(bt.batch, bt.n_kv_heads, 32768)
             nsets, steps = 2, max(10, args.steps // 3)
         elif p == "256k":
             bt = make_config(4, values=False)

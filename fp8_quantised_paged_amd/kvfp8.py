@@ -118,6 +118,15 @@ def kvfp8_attn_workspace_bytes(n_rows: int, n_q_heads: int, head_dim: int, num_s
     return int(_lib.kvfp8_attn_workspace_bytes(n_rows, n_q_heads, head_dim, num_splits))
 
 
+def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, cus: int = 256) -> int:
+    """Split count for the split kernel: enough (sequence, kv-head, split)
+    workgroups to cover the compute units about twice, with splits of at least
+    512 keys, at most 256 splits."""
+    units = max(1, batch * n_kv_heads)
+    s = max(1, -(-2 * cus // units))
+    return int(min(s, max(1, max_seq_len // 512), 256))
+
+
 def workspace(n_rows: int, n_q_heads: int, head_dim: int, num_splits: int,
               device="cuda") -> torch.Tensor:
     """An fp32 workspace tensor of the size the attention calls need."""
