@@ -51,14 +51,20 @@ def algorithmic_bytes(seq_lens, n_q_heads, n_kv_heads, head_dim, max_pages):
 class Point:
     """One decode workload resident on the GPU with `nsets` cache copies."""
 
-    def __init__(self, K, torch, name, layout, k_src, v_src, calib, num_splits, nsets):
+    def __init__(self, K, torch, name, layout, k_src, v_src, calib, num_splits, nsets, scales=None):
         self.K, self.torch, self.name, self.bt = K, torch, name, layout
         bt = layout
         dev = "cuda"
         self.S = num_splits
         self.B, self.Hq, self.Hkv, self.D, self.P = bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.page_size
-        amax, scale, _ = K.kv_calibrate_amax(calib)
-        self.ks, self.vs = float(scale[0].item()), float(scale[1].item())
+        if scales is None:
+            amax, scale, _ = K.kv_calibrate_amax(calib)
+            scales = (float(scale[0].item()), float(scale[1].item()))
+        self.ks, self.vs = scales
+        self.verify = bool((bt.q_lens != 1).any())
+        self.max_q = int(bt.q_lens.max())
+        self.rows = bt.total_q
+        self.cu_q = torch.from_numpy(bt.cu_q_lens).to(dev)
         self.sm = float(np.float32(1.0 / np.sqrt(self.D)))
         self.q = torch.from_numpy(bt.q).to(dev)
         self.block_table = torch.from_numpy(bt.block_table).to(dev)
@@ -74,8 +80,8 @@ class Point:
             vc = torch.full((bt.num_pages, self.Hkv, self.D, self.P), 0x7F, dtype=torch.uint8, device=dev)
             K.kv_quant_write(k_src, v_src, slots, self.ks, self.vs, kc, vc)
             self.sets.append((kc, vc))
-        self.ws = K.workspace(self.B, self.Hq, self.D, self.S)
-        self.ws_o, self.ws_m, self.ws_l = K.workspace_views(self.ws, self.B, self.Hq, self.D, self.S)
+        self.ws = K.workspace(self.rows, self.Hq, self.D, self.S)
+        self.ws_o, self.ws_m, self.ws_l = K.workspace_views(self.ws, self.rows, self.Hq, self.D, self.S)
         self.out = torch.empty_like(self.q)
         self.kv_bytes, self.alg_bytes = algorithmic_bytes(bt.seq_lens, self.Hq, self.Hkv, self.D,
                                                           bt.max_pages)
@@ -83,8 +89,14 @@ class Point:
 
     def attend(self, i):
         kc, vc = self.sets[i % len(self.sets)]
-        self.K.paged_attn_e4m3_decode(self.q, kc, vc, self.block_table, self.seq_lens, self.ks, self.vs,
-                                      self.sm, num_splits=self.S, workspace=self.ws, partials_only=True)
+        if self.verify:
+            self.K.paged_attn_e4m3_verify(self.q, self.cu_q, self.max_q, kc, vc, self.block_table,
+                                          self.seq_lens, self.ks, self.vs, self.sm, num_splits=self.S,
+                                          workspace=self.ws, partials_only=True)
+        else:
+            self.K.paged_attn_e4m3_decode(self.q, kc, vc, self.block_table, self.seq_lens, self.ks,
+                                          self.vs, self.sm, num_splits=self.S, workspace=self.ws,
+                                          partials_only=True)
 
     def step(self, i):
         kc, vc = self.sets[i % len(self.sets)]
@@ -155,6 +167,104 @@ class Point:
         return e0.elapsed_time(e1) / 1e3 / launches
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+
+
+def causal_pairs(seq_len, q_len):
+    """(query token, visible key) pairs of one sequence's q_len query tokens."""
+    return sum(seq_len - q_len + i + 1 for i in range(q_len))
+
+
+class MixedLayer:
+    """One layer of the mixed workload: 8 decode sequences at 8,192 keys plus one
+    2,048-token chunk over 30,000 prior keys, sharing one cache."""
+
+    def __init__(self, K, torch, scales, nsets=2):
+        from synth import make_config
+        self.K, self.torch = K, torch
+        bt = make_config(5, layer=0)
+        self.bt = bt
+        dev = "cuda"
+        self.ks, self.vs = scales
+        self.sm = float(np.float32(1.0 / np.sqrt(bt.head_dim)))
+        self.q_dec = torch.from_numpy(bt.q[:8]).to(dev)
+        self.q_chunk = torch.from_numpy(bt.q[8:]).to(dev)
+        bt_t = torch.from_numpy(bt.block_table).to(dev)
+        sl = torch.from_numpy(bt.seq_lens).to(dev)
+        self.bt_dec, self.bt_chunk = bt_t[:8].contiguous(), bt_t[8:].contiguous()
+        self.sl_dec, self.sl_chunk = sl[:8].contiguous(), sl[8:].contiguous()
+        self.cu_chunk = torch.tensor([0, 2048], dtype=torch.int32, device=dev)
+        k_src = torch.from_numpy(bt.k).to(dev)
+        v_src = torch.from_numpy(bt.v).to(dev)
+        slots = torch.from_numpy(bt.slot_mapping).to(dev)
+        new_rows = torch.from_numpy(bt.new_token_rows()).to(dev)
+        self.k_new, self.v_new = k_src[new_rows].contiguous(), v_src[new_rows].contiguous()
+        self.slots_new = slots[new_rows].contiguous()
+        self.sets = []
+        for _ in range(nsets):
+            kc = torch.full((bt.num_pages, 4, 16, 128), 0x7F, dtype=torch.uint8, device=dev)
+            vc = torch.full((bt.num_pages, 4, 128, 16), 0x7F, dtype=torch.uint8, device=dev)
+            K.kv_quant_write(k_src, v_src, slots, self.ks, self.vs, kc, vc)
+            self.sets.append((kc, vc))
+        del k_src, v_src
+        self.S = K.default_splits(8, 4, 8192)
+        self.ws = K.workspace(8, 32, 128, self.S)
+        self.ws_o, self.ws_m, self.ws_l = K.workspace_views(self.ws, 8, 32, 128, self.S)
+        self.out_dec = torch.empty_like(self.q_dec)
+        self.out_chunk = torch.empty_like(self.q_chunk)
+        self.chunk_flops = 4 * 128 * 32 * causal_pairs(32048, 2048)
+        self.dec_kv_bytes = 8 * 8192 * 4 * 128 * 2
+        torch.cuda.synchronize()
+
+    def chunk(self, i):
+        kc, vc = self.sets[i % len(self.sets)]
+        self.K.paged_attn_e4m3_verify(self.q_chunk, self.cu_chunk, 2048, kc, vc, self.bt_chunk,
+                                      self.sl_chunk, self.ks, self.vs, self.sm, out=self.out_chunk)
+
+    def step(self, i):
+        kc, vc = self.sets[i % len(self.sets)]
+        self.K.kv_quant_write(self.k_new, self.v_new, self.slots_new, self.ks, self.vs, kc, vc)
+        self.K.paged_attn_e4m3_decode(self.q_dec, kc, vc, self.bt_dec, self.sl_dec, self.ks, self.vs, self.sm,
+                                      num_splits=self.S, workspace=self.ws, partials_only=True)
+        self.K.split_reduce_fp32(self.ws_o, self.ws_m, self.ws_l, out=self.out_dec)
+        self.chunk(i)
+
+    capture = Point.capture
+
+    def time(self, steps):
+        torch = self.torch
+        n = len(self.sets)
+        g = self.capture(self.step, n)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        step_s = e0.elapsed_time(e1) / 1e3 / (reps * n)
+        gc = self.capture(self.chunk, n)
+        gc.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            gc.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        chunk_s = e0.elapsed_time(e1) / 1e3 / (reps * n)
+        return {
+            "layer_step_us": step_s * 1e6, "steps": reps * n, "chunk_kernel_us": chunk_s * 1e6,
+            "chunk_tflops": self.chunk_flops / chunk_s / 1e12,
+            "chunk_mfma_util": self.chunk_flops / chunk_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "chunk_flops": self.chunk_flops, "decode_splits": self.S,
+            "tokens_per_s_per_layer": (8 + 2048) / step_s,
+            "24_layer_step_ms": 24 * step_s * 1e3,
+        }
+
+
+
 def cpu_baseline(seconds_target=10.0):
     """The fp64 oracle timed on host cores over sampled sequences of the 4k
     decode workload (same seeded inputs as the GPU run)."""
@@ -199,7 +309,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--points", default="4k,32k,256k")
+    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed")
     ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=60)
@@ -236,6 +346,33 @@ def main():
             calib = cal.view(2, -1)
             S = K.default_splits(bt.batch, bt.n_kv_heads, 32768)
             nsets, steps = 2, max(10, args.steps // 3)
+        elif p == "mtp3":
+            bt = make_config(3)
+            k_src = torch.from_numpy(bt.k).cuda()
+            v_src = torch.from_numpy(bt.v).cuda()
+            calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
+            S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()))
+            nsets, steps = 2, max(10, args.steps // 3)
+        elif p == "mixed":
+            from synth.workloads import make_mixed_calibration
+            calib = torch.from_numpy(make_mixed_calibration()).cuda()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            amax, scale, _ = K.kv_calibrate_amax(calib)
+            e1.record()
+            torch.cuda.synchronize()
+            cal_us = e0.elapsed_time(e1) * 1e3
+            scales = (float(scale[0].item()), float(scale[1].item()))
+            del calib
+            ml = MixedLayer(K, torch, scales)
+            r = ml.time(max(10, args.steps // 3))
+            r["calibration_us_48_tensors"] = cal_us
+            r["calibration_gbs"] = 48 * 4096 * 512 * 2 / (cal_us * 1e-6) / 1e9
+            results[p] = r
+            log(f"{p}: {json.dumps(r)}")
+            del ml
+            torch.cuda.empty_cache()
+            continue
         elif p == "256k":
             bt = make_config(4, values=False)
             total = int(bt.cu_seq_lens[-1])
@@ -257,10 +394,11 @@ def main():
         launches = max(launches // nsets, 1) * nsets
         kern = pt.time_attention_kernel(launches)
         results[p] = {
-            "batch": pt.B, "seq_len": int(bt.seq_lens[0]), "num_splits": S, "page_size": pt.P,
+            "batch": pt.B, "seq_len": int(bt.seq_lens.max()), "num_splits": S, "page_size": pt.P,
+            "query_rows": pt.rows,
             "steps": steps, "ms_per_step": sec * 1e3, "host_ms_per_step": wall * 1e3,
             "kv_bytes_per_step": pt.kv_bytes, "algorithmic_bytes_per_step": pt.alg_bytes,
-            "kv_gbs": pt.kv_bytes / sec / 1e9, "tokens_per_s_per_layer": pt.B / sec,
+            "kv_gbs": pt.kv_bytes / sec / 1e9, "tokens_per_s_per_layer": pt.rows / sec,
             "attn_kernel_us": kern * 1e6, "attn_kernel_gbs": pt.alg_bytes / kern / 1e9,
             "graph_replay_matches_eager": same, "cache_sets": nsets,
         }
@@ -292,7 +430,8 @@ def main():
                    "page_size": main["page_size"], "num_splits": main["num_splits"],
                    "kv_cache": "e4m3 (OCP), per-layer K/V scales", "accumulate": "f32"},
         "pct_hbm_peak": 100.0 * main["kv_gbs"] / HBM_PEAK_GBS,
-        "tokens_per_s_per_layer": {p: r["tokens_per_s_per_layer"] for p, r in results.items()},
+        "tokens_per_s_per_layer": {p: r["tokens_per_s_per_layer"] for p, r in results.items()
+                                   if p in ("4k", "32k", "256k")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "attn_split_kernel<128,16,1,4>", "kernel_us": main["attn_kernel_us"]},

@@ -1,25 +1,31 @@
 // Reduction of FP32 split partials (o, m, l) into the fp16 output and the
-// log-sum-exp. One wavefront per (row, head); the split weights go through LDS.
+// log-sum-exp. One workgroup of four wavefronts per (row, head): every
+// wavefront forms the split weights, takes a quarter of the splits for the
+// weighted sum of o with its loads batched ahead of use, and the four partial
+// sums meet in LDS.
 #include "kvfp8_internal.h"
 
 namespace kvfp8 {
 namespace {
 
 constexpr int kMaxSplits = 256;
-constexpr int kWavesPerBlock = 4;
+constexpr int kWaves = 4;
+constexpr int kBatch = 4;  // splits whose o loads are in flight together per wavefront
 
 template <int D>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void split_reduce_kernel(
+__global__ __launch_bounds__(64 * kWaves) void split_reduce_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     int64_t n_units, int num_splits, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float wsh[kWavesPerBlock][kMaxSplits];
+  constexpr int PER = D / 64;  // dims per lane
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float part[kWaves][D];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + wave;  // (row, head)
-  if (unit >= n_units) return;  // whole wave exits together; no block barrier below
+  const int64_t unit = blockIdx.x;  // (row, head)
   const float* m = ws_m + unit * num_splits;
   const float* l = ws_l + unit * num_splits;
 
+  // global max over the splits (every wavefront computes it; it is tiny)
   float mx = -INFINITY;
   for (int s = lane; s < num_splits; s += 64) mx = fmaxf(mx, m[s]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -27,40 +33,49 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void split_reduce_kernel(
 
   float den = 0.0f;
   for (int s = lane; s < num_splits; s += 64) {
-    float ms = m[s];
-    float w = (ms == -INFINITY) ? 0.0f : __expf(ms - ref);
-    wsh[wave][s] = w;
+    const float ms = m[s];
+    const float w = (ms == -INFINITY) ? 0.0f : __expf(ms - ref);
+    if (wave == 0) wsh[s] = w;
     den += w * l[s];
   }
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __syncthreads();
 
-  constexpr int PER = D / 64;  // dims per lane
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
   const float* o = ws_o + unit * (int64_t)num_splits * D + lane * PER;
-  for (int s = 0; s < num_splits; ++s) {
-    float w = wsh[wave][s];
-    if (w != 0.0f) {
-      if constexpr (PER == 2) {
-        f32x2 v = *reinterpret_cast<const f32x2*>(o + (int64_t)s * D);
-        acc[0] += w * v[0];
-        acc[1] += w * v[1];
-      } else {
-        acc[0] += w * o[(int64_t)s * D];
-      }
+  for (int s0 = wave * kBatch; s0 < num_splits; s0 += kWaves * kBatch) {
+    float v[kBatch][PER];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = min(s0 + u, num_splits - 1);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[u][j] = o[(int64_t)s * D + j];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = (s0 + u < num_splits) ? wsh[s0 + u] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] += (w != 0.0f) ? w * v[u][j] : 0.0f;
     }
   }
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  uint16_t* dst = out + unit * D + lane * PER;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    _Float16 h = (_Float16)(den > 0.0f ? acc[j] * inv : 0.0f);
-    dst[j] = __builtin_bit_cast(uint16_t, h);
+  for (int j = 0; j < PER; ++j) part[wave][lane * PER + j] = acc[j];
+  __syncthreads();
+  if (wave == 0) {
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    uint16_t* dst = out + unit * D + lane * PER;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) t += part[w][lane * PER + j];
+      const _Float16 h = (_Float16)(den > 0.0f ? t * inv : 0.0f);
+      dst[j] = __builtin_bit_cast(uint16_t, h);
+    }
+    if (lse != nullptr && lane == 0) lse[unit] = den > 0.0f ? ref + __logf(den) : -INFINITY;
   }
-  if (lse != nullptr && lane == 0) lse[unit] = den > 0.0f ? ref + __logf(den) : -INFINITY;
 }
 
 }  // namespace
@@ -71,8 +86,8 @@ hipError_t launch_split_reduce(const float* ws_o, const float* ws_m, const float
                                hipStream_t stream) {
   int64_t units = (int64_t)n_rows * n_q_heads;
   if (units == 0) return hipSuccess;
-  dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
-  dim3 block(64 * kWavesPerBlock);
+  dim3 grid((unsigned)units);
+  dim3 block(64 * kWaves);
   if (head_dim == 128)
     split_reduce_kernel<128><<<grid, block, 0, stream>>>(ws_o, ws_m, ws_l, units, num_splits, out, lse);
   else
