@@ -230,7 +230,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
 }
 
 template <int D, int P, int NB, int W>
-__global__ __launch_bounds__(64 * W, (NB == 1 ? 2 : 1)) void attn_split_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a) {
   constexpr int NC = D / 32;
   constexpr int NBLK = D / 16;
   constexpr int ROWS = NB * 16;
@@ -302,28 +302,47 @@ __global__ __launch_bounds__(64 * W, (NB == 1 ? 2 : 1)) void attn_split_kernel(c
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
   const int last = L > 0 ? (L - 1) / P : 0;
 
-  // ---- tiles: two register buffers (the next tile's K/V in flight while the
-  // current one is computed) and two page-id sets (ids two tiles ahead)
+  // ---- tiles. With one 16-row block (decode) two register buffers keep the
+  // next tile's K/V in flight while the current one is computed, and page ids
+  // are fetched two tiles ahead; with two blocks (verify) the accumulators
+  // leave room for one buffer only, and the second wavefront per SIMD covers
+  // the latency instead.
   int it = wave;
-  if (it < ntiles) {
-    TileRegs<D, P> ra, rb;
-    PageRegs<P> pa, pb;
-    load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
-    if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-    load_tile<D, P>(ra, pa, start + it * kTile, end, L, n, g, kbase, vbase, page_stride);
-    while (true) {
-      if (it + 2 * W < ntiles) load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
-      if (it + W < ntiles)
-        load_tile<D, P>(rb, pb, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
-      compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
-      it += W;
-      if (it >= ntiles) break;
-      if (it + 2 * W < ntiles) load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
-      if (it + W < ntiles)
-        load_tile<D, P>(ra, pa, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
-      compute_tile<D, P, NB>(rb, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
-      it += W;
-      if (it >= ntiles) break;
+  if constexpr (NB == 1) {
+    if (it < ntiles) {
+      TileRegs<D, P> ra, rb;
+      PageRegs<P> pa, pb;
+      load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+      if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+      load_tile<D, P>(ra, pa, start + it * kTile, end, L, n, g, kbase, vbase, page_stride);
+      while (true) {
+        if (it + 2 * W < ntiles) load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
+        if (it + W < ntiles)
+          load_tile<D, P>(rb, pb, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
+        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+        it += W;
+        if (it >= ntiles) break;
+        if (it + 2 * W < ntiles) load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
+        if (it + W < ntiles)
+          load_tile<D, P>(ra, pa, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
+        compute_tile<D, P, NB>(rb, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+        it += W;
+        if (it >= ntiles) break;
+      }
+    }
+  } else {
+    if (it < ntiles) {
+      PageRegs<P> pa, pb;
+      load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+      while (true) {
+        TileRegs<D, P> ra;
+        load_tile<D, P>(ra, pa, start + it * kTile, end, L, n, g, kbase, vbase, page_stride);
+        if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+        it += W;
+        if (it >= ntiles) break;
+        pa = pb;
+      }
     }
   }
 

@@ -118,13 +118,20 @@ def kvfp8_attn_workspace_bytes(n_rows: int, n_q_heads: int, head_dim: int, num_s
     return int(_lib.kvfp8_attn_workspace_bytes(n_rows, n_q_heads, head_dim, num_splits))
 
 
-def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, cus: int = 256) -> int:
-    """Split count for the split kernel: enough (sequence, kv-head, split)
-    workgroups to cover the compute units about twice, with splits of at least
-    512 keys, at most 256 splits."""
-    units = max(1, batch * n_kv_heads)
-    s = max(1, -(-2 * cus // units))
-    return int(min(s, max(1, max_seq_len // 512), 256))
+def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Optional[int] = None,
+                   cus: int = 256) -> int:
+    """Split count for the split kernel (host-side heuristic).
+
+    Aims for about two workgroups per compute unit with equal work: the keys
+    of all sequences (total_keys, the sum of the context lengths, when the
+    caller knows it; batch * max_seq_len otherwise) are divided into 2 * cus
+    shares, and the longest sequence is split into shares of that size. Splits
+    hold at least 512 keys; at most 256 splits."""
+    slots = 2 * cus
+    total = (total_keys if total_keys is not None else batch * max_seq_len) * max(1, n_kv_heads)
+    share = max(512, -(-total // slots))
+    s = -(-max(1, max_seq_len) // share)
+    return int(max(1, min(s, 256)))
 
 
 def workspace(n_rows: int, n_q_heads: int, head_dim: int, num_splits: int,
