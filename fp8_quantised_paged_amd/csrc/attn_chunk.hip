@@ -39,11 +39,6 @@ __device__ __forceinline__ float wave_max_groups(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_sum_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
 
 // Raw bytes of one tile held by one thread: 16 K bytes (16 dims of one key) and
 // 16 V bytes (16 keys of one dim).
@@ -113,8 +108,12 @@ __device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const Chunk
     const int seg = tid % KSEG;
     f16x8 a = e4m3x8_to_f16(r.k[0], r.k[1]);
     f16x8 b = e4m3x8_to_f16(r.k[2], r.k[3]);
-    *reinterpret_cast<f16x8*>(&s.k[buf][kk][16 * seg]) = a;
-    *reinterpret_cast<f16x8*>(&s.k[buf][kk][16 * seg + 8]) = b;
+    // key kk is MFMA row m = 4*(kk/16) + kk%4 of M-tile t = (kk/4)%4; storing it
+    // at LDS row 16t + m makes each QK operand read 16 consecutive rows, which
+    // the padded row stride spreads over distinct banks
+    const int row = 16 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
+    *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg]) = a;
+    *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg + 8]) = b;
   }
   if (tid < D * 4) {
     const int d = tid >> 2;
@@ -198,12 +197,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
     wave_lim = first < nrows ? L - T + first / G + 1 : 0;
   }
 
-  float m_run[kNB], l_run[kNB];
+  float m_run[kNB];
+  f32x4 lacc[kNB];  // row sums of P, accumulated on the matrix core (A = ones)
   f32x4 o[kNB][NBLK];
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     m_run[nb] = -INFINITY;
-    l_run[nb] = 0.0f;
+    lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -212,7 +213,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
   const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;
   const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
-  const int krel = 16 * (n >> 2) + (n & 3);
 
   ChunkRegs regs;
   if (ntiles > 0) {
@@ -226,59 +226,68 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
     const int t0 = it * kTile;
     if (it + 1 < ntiles) chunk_load<D, P>(regs, tid, t0 + kTile, L, btrow, kbase, vbase, page_stride);
 
-    // ---- S^T = K Q^T from LDS
+    // ---- S^T = K Q^T from LDS (raw dot products of the decoded codes)
     f32x4 sc[4][kNB];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) sc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const _Float16* krow = &sm.k[buf][krel + 4 * t][16 * g];
+      const _Float16* krow = &sm.k[buf][16 * t + n][16 * g];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 64 * (c >> 1) + 8 * (c & 1));
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[nb][c], sc[t][nb], 0, 0, 0);
+          sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              ka, qb[nb][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[t][nb], 0, 0, 0);
       }
     }
-    // ---- online softmax (log2 units)
+    // ---- online softmax in log2 units; the scale is positive, so the max is
+    // taken on raw scores and the scale folds into the exponent's FMA
     const bool masked = (t0 + kTile > wave_lim);
-    f16x8 pk[kNB][2];
+    u32x4 pk[kNB][2];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       float tmax = -INFINITY;
+      if (masked) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = t0 + 16 * g + 4 * t + i;
-          float v = sc[t][nb][i] * a.score_scale;
-          if (masked) v = tok < lim[nb] ? v : -INFINITY;
-          sc[t][nb][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = wave_max_groups(tmax);
-      const float m_new = fmaxf(m_run[nb], tmax);
-      const bool none = (m_new == -INFINITY);
-      const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
-      const float mref = none ? 0.0f : m_new;
+          for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + 16 * g + 4 * t + i;
+            const float v = tok < lim[nb] ? sc[t][nb][i] : -INFINITY;
+            sc[t][nb][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][nb][i]);
+      }
+      tmax = wave_max_groups(tmax) * a.score_scale;
+      const float m_old = m_run[nb];
+      const float m_new = fmaxf(m_old, tmax);
+      const float mref = (m_new == -INFINITY) ? 0.0f : m_new;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_old) != 0) {
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
+        lacc[nb] *= alpha;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+      }
       m_run[nb] = m_new;
-      float lsum = 0.0f;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 2 * u + (j >> 2);
-          const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(sc[t][nb][j & 3] - mref);
-          pk[nb][u][j] = p;
-          lsum += (float)p;
+        for (int j = 0; j < 4; ++j) {
+          const int t = 2 * u + (j >> 1);
+          const int i = 2 * (j & 1);
+          f32x2 pp;
+          pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i], a.score_scale, -mref));
+          pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i + 1], a.score_scale, -mref));
+          pk[nb][u][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, f16x2));
         }
       }
-      l_run[nb] = l_run[nb] * alpha + lsum;
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
     }
-    // ---- O^T += V^T P^T from LDS
+    // ---- O^T += V^T P^T and l += 1^T P^T from LDS
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
 #pragma unroll
@@ -286,9 +295,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
         const f16x8 va = *reinterpret_cast<const f16x8*>(&sm.v[buf][16 * blk + n][16 * g + 8 * u]);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pk[nb][u], o[nb][blk], 0, 0, 0);
+          o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(f16x8, pk[nb][u]),
+                                                             o[nb][blk], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, __builtin_bit_cast(f16x8, pk[nb][u]),
+                                                         lacc[nb], 0, 0, 0);
     if (it + 1 < ntiles) chunk_store<D>(sm, buf ^ 1, regs, tid, t0 + kTile, L);
     __syncthreads();
   }
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
   // ---- normalise and write fp16 rows (lane holds dims 16*blk + 4g + i of row n)
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    const float lrow = wave_sum_groups(l_run[nb]);
+    const float lrow = lacc[nb][0];
     const int rr = row0 + wave * (kNB * 16) + nb * 16 + n;
     if (rr >= nrows) continue;
     const int i = rr / G;
