@@ -31,6 +31,25 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+
+# HBM bytes per launch of the 4k decode attention kernel from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs (`bench.py --counter-pass`), scaled by the same
+# counters' reading of a 1 GiB device copy. Valid only for the kernel source
+# they were taken on (sha256 prefix); otherwise the traffic is reported as null.
+MEASURED_TRAFFIC = {"source_sha256_prefix": "98f1f31ba8d79fb9", "read_bytes": 136885265,
+                    "write_bytes": 3276800}
+
+
+def measured_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "fp8_quantised_paged_amd", "csrc", "attn_split.hip")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if sha != MEASURED_TRAFFIC["source_sha256_prefix"]:
+        return None
+    return MEASURED_TRAFFIC["read_bytes"] + MEASURED_TRAFFIC["write_bytes"]
 METRIC = "decode attention KV GB/s & % of HBM peak; tokens/s per layer at 4k/32k/256k"
 
 
@@ -304,6 +323,31 @@ def cpu_baseline(seconds_target=10.0):
     }
 
 
+COPY_BYTES = 1 << 30
+
+
+def counter_pass(K, torch, make_config):
+    """Eager, unprofiled-timing launches for `rocprofv3 --pmc` runs. The copy
+    reads and writes exactly COPY_BYTES, so its FETCH_SIZE / WRITE_SIZE readings
+    give the scale from counter units to bytes."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    bt = make_config(2)
+    k_src = torch.from_numpy(bt.k).cuda()
+    v_src = torch.from_numpy(bt.v).cuda()
+    calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
+    S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)
+    pt = Point(K, torch, "4k", bt, k_src, v_src, calib, S, 6)
+    for i in range(12):
+        pt.attend(i)
+    torch.cuda.synchronize()
+    log(f"counter pass: copy {COPY_BYTES} B x3, 12 attention launches (splits {S})")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +357,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=60)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="eager launches for hardware-counter runs: a 1 GiB device copy "
+                         "(reference for the byte counters), then 4k decode attention launches")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
@@ -325,6 +372,9 @@ def main():
     from synth.device import normal_kv
 
     torch.cuda.set_device(0)
+    if args.counter_pass:
+        counter_pass(K, torch, make_config)
+        return
     points = [p for p in args.points.split(",") if p]
     results = {}
 
@@ -433,7 +483,7 @@ def main():
         "tokens_per_s_per_layer": {p: r["tokens_per_s_per_layer"] for p, r in results.items()
                                    if p in ("4k", "32k", "256k")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "attn_split_kernel<128,16,1,4>", "kernel_us": main["attn_kernel_us"]},
         "cpu_baseline": cpu,
         "points": results,
