@@ -106,22 +106,25 @@ class Point:
                                                           bt.max_pages)
         torch.cuda.synchronize()
 
-    def attend(self, i):
+    def _call(self, i, out):
         kc, vc = self.sets[i % len(self.sets)]
+        kw = dict(num_splits=self.S, workspace=self.ws)
+        kw.update(out=out) if out is not None else kw.update(partials_only=True)
         if self.verify:
             self.K.paged_attn_e4m3_verify(self.q, self.cu_q, self.max_q, kc, vc, self.block_table,
-                                          self.seq_lens, self.ks, self.vs, self.sm, num_splits=self.S,
-                                          workspace=self.ws, partials_only=True)
+                                          self.seq_lens, self.ks, self.vs, self.sm, **kw)
         else:
             self.K.paged_attn_e4m3_decode(self.q, kc, vc, self.block_table, self.seq_lens, self.ks,
-                                          self.vs, self.sm, num_splits=self.S, workspace=self.ws,
-                                          partials_only=True)
+                                          self.vs, self.sm, **kw)
+
+    def attend(self, i):
+        """The attention kernel alone (partials only)."""
+        self._call(i, None)
 
     def step(self, i):
         kc, vc = self.sets[i % len(self.sets)]
         self.K.kv_quant_write(self.k_new, self.v_new, self.slots_new, self.ks, self.vs, kc, vc)
-        self.attend(i)
-        self.K.split_reduce_fp32(self.ws_o, self.ws_m, self.ws_l, out=self.out)
+        self._call(i, self.out)
 
     def capture(self, fn, count):
         torch = self.torch
@@ -244,8 +247,7 @@ class MixedLayer:
         kc, vc = self.sets[i % len(self.sets)]
         self.K.kv_quant_write(self.k_new, self.v_new, self.slots_new, self.ks, self.vs, kc, vc)
         self.K.paged_attn_e4m3_decode(self.q_dec, kc, vc, self.bt_dec, self.sl_dec, self.ks, self.vs, self.sm,
-                                      num_splits=self.S, workspace=self.ws, partials_only=True)
-        self.K.split_reduce_fp32(self.ws_o, self.ws_m, self.ws_l, out=self.out_dec)
+                                      num_splits=self.S, workspace=self.ws, out=self.out_dec)
         self.chunk(i)
 
     capture = Point.capture

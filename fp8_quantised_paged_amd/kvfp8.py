@@ -136,9 +136,16 @@ def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Op
 
 def workspace(n_rows: int, n_q_heads: int, head_dim: int, num_splits: int,
               device="cuda") -> torch.Tensor:
-    """An fp32 workspace tensor of the size the attention calls need."""
+    """An fp32 workspace of the size the attention calls need."""
     nbytes = kvfp8_attn_workspace_bytes(n_rows, n_q_heads, head_dim, num_splits)
-    return torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=device)
+    return torch.zeros(max(nbytes // 4, 1), dtype=torch.float32, device=device)
+
+
+def poison_partials(ws: torch.Tensor, n_rows: int, n_q_heads: int, head_dim: int, num_splits: int):
+    """Fill the partials (not the counters) with NaN, so that any partial the
+    reduction reads without it having been written shows up in the output."""
+    for t in workspace_views(ws, n_rows, n_q_heads, head_dim, num_splits):
+        t.fill_(float("nan"))
 
 
 def workspace_views(ws: torch.Tensor, n_rows: int, n_q_heads: int, head_dim: int, num_splits: int):

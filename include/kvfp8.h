@@ -76,8 +76,8 @@ const char* kvfp8_last_error(void);
  *   ws_l [n_rows][n_q_heads][num_splits]            sum of exp(score - m)
  * An empty split holds m = -inf, l = 0, o = 0. The workspace is FP32 by
  * contract ([P1] Status and history and [P3] Problem and resulting behavior:
- * a half-precision split temporary broke the E4M3 route). Returns 0 for
- * non-positive arguments. */
+ * a half-precision split temporary broke the E4M3 route). Calls sharing one
+ * workspace must not overlap. Returns 0 for non-positive arguments. */
 size_t kvfp8_attn_workspace_bytes(int64_t n_rows, int32_t n_q_heads, int32_t head_dim,
                                   int32_t num_splits);
 

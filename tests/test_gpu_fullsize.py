@@ -63,7 +63,7 @@ def _decode(K, db, bt, sc, S):
     sm = np.float32(1.0 / np.sqrt(bt.head_dim))
     ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
     if ws is not None:
-        ws.fill_(float("nan"))
+        K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
     out = K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, float(sc[0]),
                                    float(sc[1]), float(sm), num_splits=S, workspace=ws)
     return out.cpu().numpy(), sm
@@ -94,7 +94,7 @@ def test_mtp3_verify_full(K):
     S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()))
     sm = np.float32(1.0 / np.sqrt(bt.head_dim))
     ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S)
-    ws.fill_(float("nan"))
+    K.poison_partials(ws, bt.total_q, bt.n_q_heads, bt.head_dim, S)
     out = K.paged_attn_e4m3_verify(db.q, db.cu_q, 4, db.k_cache, db.v_cache, db.block_table, db.seq_lens,
                                    float(sc[0]), float(sc[1]), float(sm), num_splits=S, workspace=ws)
     out = out.cpu().numpy()

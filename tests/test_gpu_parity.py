@@ -148,8 +148,8 @@ def test_quant_write_skips_padding_and_saturates(K):
 def _run_decode(K, db, ks, vs, sm, S):
     bt = db.bt
     ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
-    if ws is not None:
-        ws.fill_(float("nan"))  # every partial the reduce reads must have been written
+    if ws is not None:  # every partial the reduction reads must have been written
+        K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
     return K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens,
                                     float(ks), float(vs), float(sm), num_splits=S, workspace=ws)
 
@@ -158,7 +158,7 @@ def _run_verify(K, db, ks, vs, sm, S):
     bt = db.bt
     ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
     if ws is not None:
-        ws.fill_(float("nan"))
+        K.poison_partials(ws, bt.total_q, bt.n_q_heads, bt.head_dim, S)
     return K.paged_attn_e4m3_verify(db.q, db.cu_q, int(bt.q_lens.max()), db.k_cache, db.v_cache,
                                     db.block_table, db.seq_lens, float(ks), float(vs), float(sm),
                                     num_splits=S, workspace=ws)
@@ -218,7 +218,7 @@ def test_partials_match_oracle_partials(K):
     S = 4
     sm = sm_of(bt)
     ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
-    ws.fill_(float("nan"))
+    K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
     K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, float(sc[0]),
                              float(sc[1]), float(sm), num_splits=S, workspace=ws, partials_only=True)
     o, m, l = [t.cpu().numpy().astype(np.float64) for t in K.workspace_views(ws, bt.batch, bt.n_q_heads,
@@ -386,3 +386,66 @@ def test_chunk_rows_match_split_kernel_rows(K):
                                        float(sc[1]), float(sm)).cpu().numpy()
         err, _ = report(chunk[i], dec[0].astype(np.float64))
         assert err <= 2e-3, (i, err)
+
+
+# ----------------------------------------------------------------- fused reduce, counters, graphs
+
+@pytest.mark.parametrize("S", [16, 17, 64])
+def test_many_splits(K, S):
+    """Long and short sequences split 16 to 64 ways (many empty splits for the
+    short ones), merged by the reduce kernel."""
+    bt = make_batch([3000, 1025, 70], [1, 1, 1], 32, 4, 128, 16, seed=101)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = sm_of(bt)
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
+    K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
+    out = K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, float(sc[0]),
+                                   float(sc[1]), float(sm), num_splits=S, workspace=ws).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"S={S}")
+
+
+def test_graph_replays_match_eager(K):
+    """A captured decode step (write, split attention, reduce) replayed
+    several times, with eager work and synchronisations in between, reproduces
+    the eager output bit for bit on every replay."""
+    bt = make_batch([900, 450, 2000, 64], [1] * 4, 32, 4, 128, 16, seed=102)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    sm = float(sm_of(bt))
+    S = 4
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
+    out = torch.empty_like(db.q)
+    new = dev(bt.new_token_rows())
+    k_new, v_new, s_new = db.k[new].contiguous(), db.v[new].contiguous(), db.slots[new].contiguous()
+
+    def step():
+        K.kv_quant_write(k_new, v_new, s_new, float(sc[0]), float(sc[1]), db.k_cache, db.v_cache)
+        K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, float(sc[0]),
+                                 float(sc[1]), sm, num_splits=S, workspace=ws, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+        _ = (db.q.float() * 2).sum().item()  # unrelated eager work between replays
+        step()  # and an eager call sharing the workspace
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
