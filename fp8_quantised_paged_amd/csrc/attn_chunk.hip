@@ -5,7 +5,8 @@
 // head-in-group) of one (sequence, kv-head) and walks the keys visible to them
 // in 64-key tiles. Every tile is loaded from HBM once per workgroup, decoded
 // from E4M3 to fp16 once, and staged in LDS (K token-major, V dimension-major,
-// double-buffered so the next tile's loads overlap the current tile's math).
+// three buffers: the tile being finished, the next tile whose QK products are
+// already running, and the one after that being stored).
 // Each wavefront then computes S^T = K Q^T and O^T += V^T P^T for its 32 rows
 // with v_mfma_f32_16x16x32_f16, exactly as the split kernel does per lane (the
 // same key permutation makes the QK accumulators the PV B operand).
@@ -29,8 +30,8 @@ template <int D>
 struct ChunkLds {
   static constexpr int KS = D + 8;           // fp16 row stride of K (keys x dims)
   static constexpr int VS = kTile + 8;       // fp16 row stride of V^T (dims x keys)
-  _Float16 k[2][kTile][KS];
-  _Float16 v[2][D][VS];
+  _Float16 k[3][kTile][KS];
+  _Float16 v[3][D][VS];
 };
 
 __device__ __forceinline__ float wave_max_groups(float x) {
@@ -134,6 +135,110 @@ __device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const Chunk
   }
 }
 
+// S^T = K Q^T of one tile for this wavefront's rows (raw dot products).
+template <int D>
+__device__ __forceinline__ void chunk_qk(const ChunkLds<D>& sm, int buf, int n, int g,
+                                         const f16x8 (&qb)[kNB][D / 32], f32x4 (&sc)[4][kNB]) {
+  constexpr int NC = D / 32;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const _Float16* krow = &sm.k[buf][16 * t + n][16 * g];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 64 * (c >> 1) + 8 * (c & 1));
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            ka, qb[nb][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[t][nb], 0, 0, 0);
+    }
+  }
+}
+
+// Online softmax of one tile (log2 units; the positive scale is applied to
+// the raw max and folded into the exponent's FMA). Produces the fp16
+// probabilities packed as the PV B operand and rescales o / lacc when a row
+// max moved.
+template <int D>
+__device__ __forceinline__ void chunk_softmax(f32x4 (&sc)[4][kNB], int t0, int g, bool masked,
+                                              const int (&lim)[kNB], float score_scale,
+                                              float (&m_run)[kNB], f32x4 (&lacc)[kNB],
+                                              f32x4 (&o)[kNB][D / 16], u32x4 (&pk)[kNB][2]) {
+  constexpr int NBLK = D / 16;
+  float mnew[kNB], mold[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    float tmax = -INFINITY;
+    if (masked) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = t0 + 16 * g + 4 * t + i;
+          const float v = tok < lim[nb] ? sc[t][nb][i] : -INFINITY;
+          sc[t][nb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][nb][i]);
+    }
+    tmax = wave_max_groups(tmax) * score_scale;
+    mold[nb] = m_run[nb];
+    mnew[nb] = fmaxf(mold[nb], tmax);
+    const float mref = (mnew[nb] == -INFINITY) ? 0.0f : mnew[nb];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 2 * u + (j >> 1);
+        const int i = 2 * (j & 1);
+        f32x2 pp;
+        pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i], score_scale, -mref));
+        pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i + 1], score_scale, -mref));
+        pk[nb][u][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, f16x2));
+      }
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (__builtin_amdgcn_ballot_w64(mnew[nb] != mold[nb]) != 0) {
+      const float alpha = (mnew[nb] == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[nb] - mnew[nb]);
+      lacc[nb] *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+    }
+    m_run[nb] = mnew[nb];
+  }
+}
+
+// O^T += V^T P^T and l += 1^T P^T of one tile.
+template <int D>
+__device__ __forceinline__ void chunk_pv(const ChunkLds<D>& sm, int buf, int n, int g,
+                                         const u32x4 (&pk)[kNB][2], f32x4 (&lacc)[kNB],
+                                         f32x4 (&o)[kNB][D / 16]) {
+  constexpr int NBLK = D / 16;
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f16x8 va = *reinterpret_cast<const f16x8*>(&sm.v[buf][16 * blk + n][16 * g + 8 * u]);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(f16x8, pk[nb][u]),
+                                                           o[nb][blk], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+      lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, __builtin_bit_cast(f16x8, pk[nb][u]),
+                                                       lacc[nb], 0, 0, 0);
+}
+
 template <int D, int P>
 __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnArgs a) {
   constexpr int NC = D / 32;
@@ -200,7 +305,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
   float m_run[kNB];
   f32x4 lacc[kNB];  // row sums of P, accumulated on the matrix core (A = ones)
   f32x4 o[kNB][NBLK];
-  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     m_run[nb] = -INFINITY;
@@ -214,99 +318,42 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
   const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
 
+  // ---- software pipeline over tiles: the QK products of tile it+1 are
+  // issued next to the softmax of tile it, so the matrix cores have work
+  // while the vector units run the softmax
   ChunkRegs regs;
   if (ntiles > 0) {
     chunk_load<D, P>(regs, tid, 0, L, btrow, kbase, vbase, page_stride);
     chunk_store<D>(sm, 0, regs, tid, 0, L);
   }
+  if (ntiles > 1) {
+    chunk_load<D, P>(regs, tid, kTile, L, btrow, kbase, vbase, page_stride);
+    chunk_store<D>(sm, 1, regs, tid, kTile, L);
+  }
   __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int t0 = it * kTile;
-    if (it + 1 < ntiles) chunk_load<D, P>(regs, tid, t0 + kTile, L, btrow, kbase, vbase, page_stride);
-
-    // ---- S^T = K Q^T from LDS (raw dot products of the decoded codes)
-    f32x4 sc[4][kNB];
+  f32x4 sa[4][kNB], sb[4][kNB];
+  u32x4 pk[kNB][2];
+  if (ntiles > 0) chunk_qk<D>(sm, 0, n, g, qb, sa);
+  int buf = 0;  // buffer of tile it
+  for (int it = 0; it < ntiles; it += 2) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const _Float16* krow = &sm.k[buf][16 * t + n][16 * g];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 64 * (c >> 1) + 8 * (c & 1));
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              ka, qb[nb][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[t][nb], 0, 0, 0);
+    for (int half = 0; half < 2; ++half) {
+      const int t = it + half;
+      if (t < ntiles) {
+        f32x4 (&cur)[4][kNB] = half == 0 ? sa : sb;
+        f32x4 (&nxt)[4][kNB] = half == 0 ? sb : sa;
+        const int buf1 = buf == 2 ? 0 : buf + 1;
+        const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
+        if (t + 2 < ntiles) chunk_load<D, P>(regs, tid, (t + 2) * kTile, L, btrow, kbase, vbase, page_stride);
+        if (t + 1 < ntiles) chunk_qk<D>(sm, buf1, n, g, qb, nxt);
+        chunk_softmax<D>(cur, t * kTile, g, t * kTile + kTile > wave_lim, lim, a.score_scale, m_run,
+                         lacc, o, pk);
+        chunk_pv<D>(sm, buf, n, g, pk, lacc, o);
+        if (t + 2 < ntiles) chunk_store<D>(sm, buf2, regs, tid, (t + 2) * kTile, L);
+        __syncthreads();
+        buf = buf1;
       }
     }
-    // ---- online softmax in log2 units; the scale is positive, so the max is
-    // taken on raw scores and the scale folds into the exponent's FMA
-    const bool masked = (t0 + kTile > wave_lim);
-    u32x4 pk[kNB][2];
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      float tmax = -INFINITY;
-      if (masked) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = t0 + 16 * g + 4 * t + i;
-            const float v = tok < lim[nb] ? sc[t][nb][i] : -INFINITY;
-            sc[t][nb][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][nb][i]);
-      }
-      tmax = wave_max_groups(tmax) * a.score_scale;
-      const float m_old = m_run[nb];
-      const float m_new = fmaxf(m_old, tmax);
-      const float mref = (m_new == -INFINITY) ? 0.0f : m_new;
-      if (__builtin_amdgcn_ballot_w64(m_new != m_old) != 0) {
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
-        lacc[nb] *= alpha;
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
-      }
-      m_run[nb] = m_new;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 2 * u + (j >> 1);
-          const int i = 2 * (j & 1);
-          f32x2 pp;
-          pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i], a.score_scale, -mref));
-          pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i + 1], a.score_scale, -mref));
-          pk[nb][u][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, f16x2));
-        }
-      }
-    }
-    // ---- O^T += V^T P^T and l += 1^T P^T from LDS
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(&sm.v[buf][16 * blk + n][16 * g + 8 * u]);
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(f16x8, pk[nb][u]),
-                                                             o[nb][blk], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, __builtin_bit_cast(f16x8, pk[nb][u]),
-                                                         lacc[nb], 0, 0, 0);
-    if (it + 1 < ntiles) chunk_store<D>(sm, buf ^ 1, regs, tid, t0 + kTile, L);
-    __syncthreads();
   }
 
   // ---- normalise and write fp16 rows (lane holds dims 16*blk + 4g + i of row n)
