@@ -81,6 +81,9 @@ int32_t check_common(const AttnCommon& c, int64_t n_rows) {
   if (!good_scale(c.k_scale) || !good_scale(c.v_scale) || !good_scale(c.sm_scale))
     return fail(KVFP8_BAD_SCALE, "k_scale, v_scale and sm_scale must be finite, positive and normal "
                 "(got %g, %g, %g)", (double)c.k_scale, (double)c.v_scale, (double)c.sm_scale);
+  if (!good_scale(c.k_scale * c.sm_scale * kvfp8::kLog2e))
+    return fail(KVFP8_BAD_SCALE, "k_scale * sm_scale * log2(e) = %g leaves the normal fp32 range",
+                (double)(c.k_scale * c.sm_scale * kvfp8::kLog2e));
   if (!aligned16(c.q) || !aligned16(c.k_cache) || !aligned16(c.v_cache))
     return fail(KVFP8_INVALID_ARG, "q, k_cache and v_cache must be 16-byte aligned");
   if (c.out && !aligned16(c.out)) return fail(KVFP8_INVALID_ARG, "out must be 16-byte aligned");

@@ -9,17 +9,18 @@
 // Per 64-key tile a wavefront computes S^T = K Q^T and O^T += V^T P^T with
 // v_mfma_f32_16x16x32_f16:
 //  * QK: A = 16 keys x 32 dims of K (decoded from E4M3 in registers), B = the
-//    same 32 dims x 16 query rows of Q (registers for the whole kernel). The
-//    contraction order over dims is free, so MFMA c takes, in lane group g
-//    (lanes 16g..16g+15), dims 16g + 64*(c/2) + 8*(c%2) + i: each load
-//    instruction then reads 64 contiguous bytes of 16 key rows. The key of MFMA row m in M-tile t is 16*(m/4) + 4t + m%4, which puts
-//    keys 16g + 4t + i of every query row in lane group g's accumulators.
+//    same 32 dims x 16 query rows of Q (fp16, held in LDS for the workgroup).
+//    The contraction order over dims is free, so MFMA c takes, in lane group
+//    g (lanes 16g..16g+15), dims 16g + 64*(c/2) + 8*(c%2) + i: each load
+//    instruction then reads 64 contiguous bytes of 16 key rows. The key of
+//    MFMA row m in M-tile t is 16*(m/4) + 4t + m%4, which puts keys
+//    16g + 4t + i of every query row in lane group g's accumulators.
 //  * PV: A = 16 dims x 32 keys of V^T, B = the 32 keys x 16 rows of P taken
 //    straight from the QK accumulators (no cross-lane movement). Lane group g
 //    needs keys 16g .. 16g+15 of one dimension: 16 contiguous bytes of the
 //    dimension-major V page.
-// Scores are scaled once per tile by k_scale * sm_scale * log2(e); v_scale is
-// applied once to the merged accumulator.
+// Scores are scaled once per tile by k_scale * sm_scale * log2(e) (folded into
+// the exp2 argument); v_scale is applied once to the merged accumulator.
 #include "kvfp8_internal.h"
 
 namespace kvfp8 {
@@ -72,89 +73,91 @@ __device__ __forceinline__ void load_pages(PageRegs<P>& pr, const int32_t* __res
 
 // K/V bytes are read exactly once per call, so they are loaded non-temporally
 // (streamed past the caches instead of evicting the block table, Q and the
-// partials).
+// partials). The loads are unconditional: a tile never extends past the split
+// unless the split ends the sequence, and page ids are clamped to the last
+// page, so keys past the end read rows of an allocated page. Their scores are
+// masked and their V bytes cleared in compute_tile, which is cheaper than
+// branching and zero-filling the registers on every tile.
+// In-page byte offsets of this lane's K rows and V bytes. Tiles start at
+// multiples of 64 keys, so the offsets are the same for every tile.
 template <int D, int P>
-__device__ __forceinline__ void load_tile(TileRegs<D, P>& r, const PageRegs<P>& pr, int t0, int end,
-                                          int L, int n, int g, const uint8_t* __restrict__ kbase,
-                                          const uint8_t* __restrict__ vbase, int64_t page_stride) {
+struct LaneOffsets {
+  uint32_t k[4];  // K row of M-tile t, dims from 16g
+  uint32_t v;     // V bytes of dimension n, keys from 16g (piece 0)
+  __device__ __forceinline__ LaneOffsets(int n, int g) {
+    const int krel = 16 * (n >> 2) + (n & 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) k[t] = (uint32_t)(((krel + 4 * t) % P) * D + 16 * g);
+    v = (uint32_t)(n * P + (16 * g) % P);
+  }
+};
+
+template <int D, int P>
+__device__ __forceinline__ void load_tile(TileRegs<D, P>& r, const PageRegs<P>& pr, const LaneOffsets<D, P>& lo,
+                                          const uint8_t* __restrict__ kbase,
+                                          const uint8_t* __restrict__ vbase, uint32_t page_stride) {
   constexpr int KD = D / 16;  // dwords of K per lane and M-tile
   // ---- K: the key row of this lane in M-tile t is t0 + 16*(n/4) + 4t + n%4.
   // Lane group g reads dims [16g, 16g+16) (and [64+16g, 80+16g) for D = 128),
   // so each load instruction covers 64 contiguous bytes of every key row.
-  const int krel = 16 * (n >> 2) + (n & 3);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int tok = t0 + krel + 4 * t;
-    if (tok < end) {
-      const int64_t pg = pr.k[PageRegs<P>::NK == 1 ? 0 : t];
-      const uint8_t* p = kbase + pg * page_stride + (int64_t)(tok % P) * D + 16 * g;
+    const uint32_t pg = (uint32_t)pr.k[PageRegs<P>::NK == 1 ? 0 : t];
+    const uint8_t* p = kbase + (uint64_t)pg * page_stride + lo.k[t];
 #pragma unroll
-      for (int j = 0; j < KD / 4; ++j) {
-        u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
-        r.k[t][4 * j + 0] = w[0];
-        r.k[t][4 * j + 1] = w[1];
-        r.k[t][4 * j + 2] = w[2];
-        r.k[t][4 * j + 3] = w[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KD; ++j) r.k[t][j] = 0u;
+    for (int j = 0; j < KD / 4; ++j) {
+      u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64 * j));
+      r.k[t][4 * j + 0] = w[0];
+      r.k[t][4 * j + 1] = w[1];
+      r.k[t][4 * j + 2] = w[2];
+      r.k[t][4 * j + 3] = w[3];
     }
   }
   // ---- V: keys t0 + 16g .. +15 of dimensions 16*blk + n
-  const int tv = t0 + 16 * g;
   if constexpr (P >= 16) {
-    if (tv < L) {
-      const int64_t pg = pr.v[0];
-      const uint8_t* p = vbase + pg * page_stride + (int64_t)n * P + (tv % P);
+    const uint8_t* p = vbase + (uint64_t)(uint32_t)pr.v[0] * page_stride + lo.v;
 #pragma unroll
-      for (int blk = 0; blk < D / 16; ++blk) {
-        u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (int64_t)blk * 16 * P));
-        r.v[blk][0] = w[0];
-        r.v[blk][1] = w[1];
-        r.v[blk][2] = w[2];
-        r.v[blk][3] = w[3];
-      }
-    } else {
-#pragma unroll
-      for (int blk = 0; blk < D / 16; ++blk) r.v[blk][0] = r.v[blk][1] = r.v[blk][2] = r.v[blk][3] = 0u;
+    for (int blk = 0; blk < D / 16; ++blk) {
+      u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + blk * 16 * P));
+      r.v[blk][0] = w[0];
+      r.v[blk][1] = w[1];
+      r.v[blk][2] = w[2];
+      r.v[blk][3] = w[3];
     }
   } else {
     constexpr int PIECES = 16 / P;  // pages covered by 16 keys
     constexpr int PD = P / 4;       // dwords per piece
 #pragma unroll
     for (int pc = 0; pc < PIECES; ++pc) {
-      const int tp = tv + pc * P;
-      if (tp < L) {
-        const int64_t pg = pr.v[pc];
-        const uint8_t* p = vbase + pg * page_stride + (int64_t)n * P;
+      const uint8_t* p = vbase + (uint64_t)(uint32_t)pr.v[pc] * page_stride + lo.v;
 #pragma unroll
-        for (int blk = 0; blk < D / 16; ++blk) {
-          const uint8_t* q = p + (int64_t)blk * 16 * P;
-          if constexpr (PD == 2) {
-            u32x2 w = *reinterpret_cast<const u32x2*>(q);
-            r.v[blk][pc * 2 + 0] = w[0];
-            r.v[blk][pc * 2 + 1] = w[1];
-          } else {
-            r.v[blk][pc] = *reinterpret_cast<const uint32_t*>(q);
-          }
+      for (int blk = 0; blk < D / 16; ++blk) {
+        const uint8_t* q = p + blk * 16 * P;
+        if constexpr (PD == 2) {
+          u32x2 w = *reinterpret_cast<const u32x2*>(q);
+          r.v[blk][pc * 2 + 0] = w[0];
+          r.v[blk][pc * 2 + 1] = w[1];
+        } else {
+          r.v[blk][pc] = *reinterpret_cast<const uint32_t*>(q);
         }
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < D / 16; ++blk)
-#pragma unroll
-          for (int j = 0; j < PD; ++j) r.v[blk][pc * PD + j] = 0u;
       }
     }
   }
 }
 
+// Rows keep a reference maximum m_ref for their probabilities and rescale
+// their accumulators only when some row's maximum moves more than kLazy (log2
+// units) above it: probabilities are then at most 2^kLazy, which fp16 and the
+// fp32 accumulators hold exactly as well as values below 1. The true running
+// maximum m_max is tracked beside it; the state is brought to m_max once, at
+// the end.
+constexpr float kLazy = 8.0f;
+
 template <int D, int P, int NB>
 __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, int g,
-                                             const f16x8 (&qb)[NB][D / 32], const int (&lim)[NB],
-                                             float score_scale, float (&m_run)[NB],
+                                             const f16x8 (*sq)[D / 32][64], const int (&lim)[NB],
+                                             float score_scale, float (&m_ref)[NB], float (&m_max)[NB],
                                              float (&l_run)[NB], f32x4 (&o)[NB][D / 16]) {
-  constexpr int NC = D / 32;
   constexpr int NBLK = D / 16;
   // keys at or past the end of the sequence may hold poison codes: zero their
   // V bytes so that a zero probability cannot meet a NaN in the PV product
@@ -167,54 +170,76 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
       for (int blk = 0; blk < NBLK; ++blk) r.v[blk][w4] &= mask;
     }
   }
-  // ---- S^T = K Q^T
+  // ---- S^T = K Q^T. Q is re-read from LDS every tile (the empty asm keeps
+  // the compiler from hoisting it into registers, which the K/V double buffer
+  // needs).
+  __asm__ volatile("" ::: "memory");
+  const int lane = threadIdx.x & 63;
   f32x4 sc[4][NB];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+  for (int c = 0; c < D / 32; ++c) {
+    f16x8 qop[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) qop[nb] = sq[nb][c][lane];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
       f16x8 ka = e4m3x8_to_f16(r.k[t][2 * c], r.k[t][2 * c + 1]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[nb][c], sc[t][nb], 0, 0, 0);
+        sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[nb], sc[t][nb], 0, 0, 0);
     }
   }
-  // ---- online softmax (log2 units); rows are lane columns
+
+  // ---- online softmax (log2 units); rows are lane columns. The maximum is
+  // taken on raw scores (score_scale > 0) and the scale folded into exp2's FMA.
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   f16x8 pk[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
+    // mask keys at or past each row's limit (the end of the split, or the
+    // row's causal position); the compare constants are the lane's key offsets
+    {
+      const int rem = lim[nb] - t0 - 16 * g;  // keys 16g + k of the tile with k < rem are visible
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * t + i >= rem) sc[t][nb][i] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * g + 4 * t + i;
-        const float v = tok < lim[nb] ? sc[t][nb][i] * score_scale : -INFINITY;
-        sc[t][nb][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = wave_max_groups(tmax);
-    const float m_new = fmaxf(m_run[nb], tmax);
-    const bool none = (m_new == -INFINITY);
-    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
-    const float mref = none ? 0.0f : m_new;
-    m_run[nb] = m_new;
-    float lsum = 0.0f;
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][nb][i]);
+    tmax = wave_max_groups(tmax) * score_scale;
+    m_max[nb] = fmaxf(m_max[nb], tmax);
+    if (__builtin_amdgcn_ballot_w64(m_max[nb] > m_ref[nb] + kLazy) != 0) {
+      const float m_new = m_max[nb];
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+      m_ref[nb] = m_new;
+      l_run[nb] *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+    }
+    const float nref = (m_ref[nb] == -INFINITY) ? 0.0f : -m_ref[nb];
+    float lsum = l_run[nb];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int t = 2 * u + (j >> 2);
-        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(sc[t][nb][j & 3] - mref);
-        pk[nb][u][j] = p;
-        lsum += (float)p;
+        pk[nb][u][j] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][j & 3], score_scale, nref));
       }
+      lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk[nb][u], pk[nb][u], 0, 1), ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk[nb][u], pk[nb][u], 2, 3), ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk[nb][u], pk[nb][u], 4, 5), ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk[nb][u], pk[nb][u], 6, 7), ones, lsum, false);
     }
-    l_run[nb] = l_run[nb] * alpha + lsum;
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+    l_run[nb] = lsum;
   }
   // ---- O^T += V^T P^T
 #pragma unroll
@@ -238,6 +263,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   __shared__ float sm_m[W][ROWS];
   __shared__ float sm_l[W][ROWS];
   __shared__ __attribute__((aligned(16))) float sm_o[W][ROWS][OPAD];
+  __shared__ f16x8 sm_q[NB][NC][64];  // Q rows, the B operand of each lane
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -265,99 +291,111 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int end = min(start + chunk, L);
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
 
-  // ---- Q operand (dims g*D/4 + 8c + i of row n of each 16-row block)
-  f16x8 qb[NB][NC];
-  int lim[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int rr = nb * 16 + n;
-    if (rr < nrows) {
-      const int i = rr / G;
-      const int h = kvh * G + rr % G;
-      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
-      lim[nb] = min(end, L - T + i + 1);
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qb[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      lim[nb] = 0;
-    }
-  }
-
-  float m_run[NB], l_run[NB];
-  f32x4 o[NB][NBLK];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.0f;
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int64_t page_stride = (int64_t)a.n_kv_heads * P * D;
+  const uint32_t page_stride = (uint32_t)a.n_kv_heads * P * D;  // < 2^32: n_kv_heads <= 65535
+  const LaneOffsets<D, P> lo(n, g);
   const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;
   const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
   const int last = L > 0 ? (L - 1) / P : 0;
+
+  // ---- start-up: wavefront 0 loads the Q rows while every wavefront loads
+  // its first page ids, then the first tile's K/V are issued before Q goes to
+  // LDS, so the three latencies overlap instead of adding up.
+  // Q operand: dims g*D/4 + 8c + i of row n of each 16-row block.
+  f16x8 qraw[NB][NC];
+  int lim[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int rr = nb * 16 + n;
+    const int i = rr / G;
+    lim[nb] = rr < nrows ? min(end, L - T + i + 1) : 0;
+    if (wave == 0) {
+      if (rr < nrows) {
+        const int h = kvh * G + rr % G;
+        const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          qraw[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qraw[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+  int it = wave;
+  PageRegs<P> pa, pb;
+  TileRegs<D, P> ra;
+  if (it < ntiles) {
+    load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+    if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+    load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sm_q[nb][c][lane] = qraw[nb][c];
+  }
+  __syncthreads();
+
+  float m_ref[NB], m_max[NB], l_run[NB];
+  f32x4 o[NB][NBLK];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_ref[nb] = -INFINITY;
+    m_max[nb] = -INFINITY;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- tiles. With one 16-row block (decode) two register buffers keep the
   // next tile's K/V in flight while the current one is computed, and page ids
   // are fetched two tiles ahead; with two blocks (verify) the accumulators
   // leave room for one buffer only, and the second wavefront per SIMD covers
   // the latency instead.
-  int it = wave;
   if constexpr (NB == 1) {
     if (it < ntiles) {
-      TileRegs<D, P> ra, rb;
-      PageRegs<P> pa, pb;
-      load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
-      if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-      load_tile<D, P>(ra, pa, start + it * kTile, end, L, n, g, kbase, vbase, page_stride);
+      TileRegs<D, P> rb;
       while (true) {
         if (it + 2 * W < ntiles) load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
-        if (it + W < ntiles)
-          load_tile<D, P>(rb, pb, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
-        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+        if (it + W < ntiles) load_tile<D, P>(rb, pb, lo, kbase, vbase, page_stride);
+        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
         if (it + 2 * W < ntiles) load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
-        if (it + W < ntiles)
-          load_tile<D, P>(ra, pa, start + (it + W) * kTile, end, L, n, g, kbase, vbase, page_stride);
-        compute_tile<D, P, NB>(rb, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+        if (it + W < ntiles) load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
+        compute_tile<D, P, NB>(rb, start + it * kTile, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
       }
     }
   } else {
     if (it < ntiles) {
-      PageRegs<P> pa, pb;
-      load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
       while (true) {
-        TileRegs<D, P> ra;
-        load_tile<D, P>(ra, pa, start + it * kTile, end, L, n, g, kbase, vbase, page_stride);
         if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, qb, lim, a.score_scale, m_run, l_run, o);
+        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
-        pa = pb;
+        load_tile<D, P>(ra, pb, lo, kbase, vbase, page_stride);
       }
     }
   }
 
-  // ---- merge the wavefronts' states through LDS
+  // ---- bring each wavefront's state to its true maximum and merge the
+  // wavefronts' states through LDS
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float lrow = wave_sum_groups(l_run[nb]);
+    const float fac = (m_max[nb] == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_max[nb]);
+    const float lrow = wave_sum_groups(l_run[nb]) * fac;
     const int rr = nb * 16 + n;
     if (g == 0) {
-      sm_m[wave][rr] = m_run[nb];
+      sm_m[wave][rr] = m_max[nb];
       sm_l[wave][rr] = lrow;
     }
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
-      *reinterpret_cast<f32x4*>(&sm_o[wave][rr][16 * blk + 4 * g]) = o[nb][blk];
+      *reinterpret_cast<f32x4*>(&sm_o[wave][rr][16 * blk + 4 * g]) = o[nb][blk] * fac;
   }
   __syncthreads();
 

@@ -19,13 +19,14 @@ __global__ __launch_bounds__(256) void quant_write_kernel(
   const int g = (int)(idx % groups);
   const int h = (int)((idx / groups) % n_kv_heads);
   const int64_t t = idx / ((int64_t)groups * n_kv_heads);
+  // the slot and the K/V values are independent loads: issue them together
+  const int64_t src = (t * n_kv_heads + h) * head_dim + (int64_t)g * 8;
   const int64_t slot = slots[t];
+  const u32x4 kw = *reinterpret_cast<const u32x4*>(k + src);
+  const u32x4 vw = *reinterpret_cast<const u32x4*>(v + src);
   if (slot < 0 || slot >= num_pages * page_size) return;
   const int64_t page = slot / page_size;
   const int off = (int)(slot - page * page_size);
-  const int64_t src = (t * n_kv_heads + h) * head_dim + (int64_t)g * 8;
-  u32x4 kw = *reinterpret_cast<const u32x4*>(k + src);
-  u32x4 vw = *reinterpret_cast<const u32x4*>(v + src);
 
   uint32_t kc[2] = {0u, 0u};
 #pragma unroll

@@ -16,7 +16,8 @@ template <int D>
 __global__ __launch_bounds__(64 * kWaves) void split_reduce_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     int64_t n_units, int num_splits, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int PER = D / 64;  // dims per lane
+  constexpr int PER = D / 64;             // dims per lane
+  constexpr int SPL = kMaxSplits / 64;    // splits per lane for m and l
   __shared__ float wsh[kMaxSplits];
   __shared__ float part[kWaves][D];
   const int lane = threadIdx.x & 63;
@@ -24,19 +25,41 @@ __global__ __launch_bounds__(64 * kWaves) void split_reduce_kernel(
   const int64_t unit = blockIdx.x;  // (row, head)
   const float* m = ws_m + unit * num_splits;
   const float* l = ws_l + unit * num_splits;
+  const float* o = ws_o + unit * (int64_t)num_splits * D + lane * PER;
 
-  // global max over the splits (every wavefront computes it; it is tiny)
+  // Every load that does not depend on the weights is issued first: this
+  // wavefront's first batch of o, and m and l of every split, so the kernel
+  // waits for memory once rather than once per step.
+  float v[kBatch][PER];
+  int s0 = wave * kBatch;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int s = min(s0 + u, num_splits - 1);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[u][j] = o[(int64_t)s * D + j];
+  }
+  float ms[SPL], ls[SPL];
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const int s = lane + 64 * k;
+    ms[k] = s < num_splits ? m[s] : -INFINITY;
+    ls[k] = s < num_splits ? l[s] : 0.0f;
+  }
+
+  // global max and weighted normaliser over the splits (every wavefront
+  // computes them; wavefront 0 publishes the weights)
   float mx = -INFINITY;
-  for (int s = lane; s < num_splits; s += 64) mx = fmaxf(mx, m[s]);
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) mx = fmaxf(mx, ms[k]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   const float ref = (mx == -INFINITY) ? 0.0f : mx;
-
   float den = 0.0f;
-  for (int s = lane; s < num_splits; s += 64) {
-    const float ms = m[s];
-    const float w = (ms == -INFINITY) ? 0.0f : __expf(ms - ref);
-    if (wave == 0) wsh[s] = w;
-    den += w * l[s];
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const float w = (ms[k] == -INFINITY) ? 0.0f : __expf(ms[k] - ref);
+    const int s = lane + 64 * k;
+    if (wave == 0 && s < num_splits) wsh[s] = w;
+    den += w * ls[k];
   }
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
   __syncthreads();
@@ -44,20 +67,20 @@ __global__ __launch_bounds__(64 * kWaves) void split_reduce_kernel(
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
-  const float* o = ws_o + unit * (int64_t)num_splits * D + lane * PER;
-  for (int s0 = wave * kBatch; s0 < num_splits; s0 += kWaves * kBatch) {
-    float v[kBatch][PER];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int s = min(s0 + u, num_splits - 1);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) v[u][j] = o[(int64_t)s * D + j];
-    }
+  while (s0 < num_splits) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const float w = (s0 + u < num_splits) ? wsh[s0 + u] : 0.0f;
 #pragma unroll
       for (int j = 0; j < PER; ++j) acc[j] += (w != 0.0f) ? w * v[u][j] : 0.0f;
+    }
+    s0 += kWaves * kBatch;
+    if (s0 >= num_splits) break;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = min(s0 + u, num_splits - 1);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[u][j] = o[(int64_t)s * D + j];
     }
   }
 #pragma unroll

@@ -125,7 +125,8 @@ int32_t kv_quant_write(const uint16_t* k_f16, const uint16_t* v_f16, const int64
  * from several context shards). Supported: head_dim 64 or 128, page_size 4, 8,
  * 16, 32 or 64, n_q_heads a multiple of n_kv_heads with a group of at most 32
  * heads, 1 <= num_splits <= 256. q, caches, workspace and out must be 16-byte
- * aligned. k_scale, v_scale, sm_scale: finite, positive, normal fp32. */
+ * aligned. k_scale, v_scale, sm_scale: finite, positive, normal fp32, and so
+ * must be k_scale * sm_scale * log2(e) (else KVFP8_BAD_SCALE). */
 int32_t paged_attn_e4m3_decode(const uint16_t* q_f16, const uint8_t* k_cache, const uint8_t* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

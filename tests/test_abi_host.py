@@ -123,6 +123,8 @@ def decode(**kw):
     (dict(vs=0.0), kvfp8.BAD_SCALE),
     (dict(sm=-1.0), kvfp8.BAD_SCALE),
     (dict(sm=float("inf")), kvfp8.BAD_SCALE),
+    (dict(ks=1e-30, sm=1e-20), kvfp8.BAD_SCALE),  # product underflows fp32
+    (dict(ks=1e30, sm=1e20), kvfp8.BAD_SCALE),  # product overflows fp32
     (dict(q=MIS), kvfp8.INVALID_ARG),
     (dict(vc=MIS), kvfp8.INVALID_ARG),
     (dict(out=MIS), kvfp8.INVALID_ARG),

@@ -284,6 +284,42 @@ def test_single_token_context_returns_v_for_every_code(K):
             assert np.array_equal(out[b, h].astype(np.float64), ref[b, h // 2])
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_every_k_code_reaches_the_scores(K, D):
+    """Two keys per sequence: key 0 holds one K code (every non-NaN code, one
+    per kv-head) in a single dimension, key 1 is zero; V is 1 for key 0 and 0
+    for key 1, so the output is the softmax weight of key 0, a sigmoid of
+    q * decode(code) * k_scale * sm_scale. Query magnitudes from 1 to 60000
+    put every code, the E4M3 subnormals included, where the weight depends on
+    its exact value."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    n_kvh = 4
+    n_seq = -(-len(codes) // n_kvh)
+    codes = np.concatenate([codes, np.zeros(n_seq * n_kvh - len(codes), np.uint8)]).reshape(n_seq, n_kvh)
+    bt = make_batch([2] * n_seq, [1] * n_seq, 4 * n_kvh, n_kvh, D, 16, seed=86)
+    qmag = np.array([60000.0, 3000.0, 100.0, 1.0], np.float16)
+    bt.q[:] = 0
+    for h in range(4 * n_kvh):
+        bt.q[:, h, 5] = qmag[h % 4]
+    kc = np.zeros((bt.num_pages, n_kvh, 16, D), np.uint8)
+    vc = np.zeros((bt.num_pages, n_kvh, D, 16), np.uint8)
+    for b in range(n_seq):
+        page = bt.block_table[b, 0]
+        kc[page, :, 0, 5] = codes[b]
+        vc[page, :, :, 0] = 0x38  # 1.0
+    db = DeviceBatch(bt)
+    db.k_cache.copy_(dev(kc))
+    db.v_cache.copy_(dev(vc))
+    ks, vs, sm = np.float32(0.125), np.float32(1.0), np.float32(0.125)
+    out = K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, db.seq_lens, float(ks),
+                                   float(vs), float(sm)).cpu().numpy()
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, ks, vs, sm)
+    assert_close_attn(out, ref, f"every K code D={D}")
+    # the smallest subnormal code moves the weight well away from 1/2 at q = 60000
+    b1, h1 = np.argwhere(codes == 0x01)[0]
+    assert out[b1, 4 * h1, 0] > 0.8
+
+
 def test_page_permutation_bit_identical(K):
     bt = make_batch([300, 77], [1, 1], 32, 4, 128, 16, seed=82)
     _, sc = oracle_scales(bt)
