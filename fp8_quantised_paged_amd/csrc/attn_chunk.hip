@@ -48,50 +48,61 @@ struct ChunkRegs {
   u32x4 v;
 };
 
+// Page ids of one thread's K row and V keys in one tile, clamped to the
+// sequence's last page (so no block-table entry past it is read). They are
+// fetched one tile ahead of the K/V bytes: the vector memory counter is
+// in-order, and a wait on an id issued just before the bytes of another tile
+// would also wait for those bytes.
+template <int P>
+struct ChunkPages {
+  static constexpr int NV = P >= 16 ? 1 : 16 / P;
+  int32_t k;
+  int32_t v[NV];
+};
+
 template <int D, int P>
-__device__ __forceinline__ void chunk_load(ChunkRegs& r, int tid, int t0, int L,
-                                           const int32_t* __restrict__ btrow,
-                                           const uint8_t* __restrict__ kbase,
-                                           const uint8_t* __restrict__ vbase, int64_t page_stride) {
+__device__ __forceinline__ void chunk_pages(ChunkPages<P>& pg, int tid, int t0, int last,
+                                            const int32_t* __restrict__ btrow) {
   constexpr int KSEG = D / 16;  // 16-byte segments per key row
-  const int last = (L - 1) / P;
-  r.k = u32x4{0u, 0u, 0u, 0u};
-  r.v = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kTile * KSEG) pg.k = btrow[min((t0 + tid / KSEG) / P, last)];
+  if (tid < D * 4) {
+    const int tv = t0 + 16 * (tid & 3);
+#pragma unroll
+    for (int pc = 0; pc < ChunkPages<P>::NV; ++pc) pg.v[pc] = btrow[min((tv + pc * P) / P, last)];
+  }
+}
+
+// Unconditional loads: keys past the end of the sequence read rows of the
+// (clamped) last page; their scores are masked and their V bytes cleared in
+// chunk_store.
+template <int D, int P>
+__device__ __forceinline__ void chunk_load(ChunkRegs& r, const ChunkPages<P>& pg, int tid, int t0,
+                                           const uint8_t* __restrict__ kbase,
+                                           const uint8_t* __restrict__ vbase, uint32_t page_stride) {
+  constexpr int KSEG = D / 16;
   if (tid < kTile * KSEG) {
     const int kk = tid / KSEG;
     const int seg = tid % KSEG;
-    const int tok = t0 + kk;
-    if (tok < L) {
-      const int64_t pg = btrow[min(tok / P, last)];
-      r.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          kbase + pg * page_stride + (int64_t)(tok % P) * D + 16 * seg));
-    }
+    const uint32_t off = (uint32_t)(((t0 + kk) % P) * D + 16 * seg);
+    r.k = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(kbase + (uint64_t)(uint32_t)pg.k * page_stride + off));
   }
   if (tid < D * 4) {
     const int d = tid >> 2;
-    const int kseg = tid & 3;
-    const int tv = t0 + 16 * kseg;
+    const int tv = t0 + 16 * (tid & 3);
     if constexpr (P >= 16) {
-      if (tv < L) {
-        const int64_t pg = btrow[min(tv / P, last)];
-        r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            vbase + pg * page_stride + (int64_t)d * P + (tv % P)));
-      }
+      r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          vbase + (uint64_t)(uint32_t)pg.v[0] * page_stride + (uint32_t)(d * P + tv % P)));
     } else {
-      constexpr int PIECES = 16 / P;
 #pragma unroll
-      for (int pc = 0; pc < PIECES; ++pc) {
-        const int tp = tv + pc * P;
-        if (tp < L) {
-          const int64_t pg = btrow[min(tp / P, last)];
-          const uint8_t* q = vbase + pg * page_stride + (int64_t)d * P;
-          if constexpr (P == 8) {
-            u32x2 w = *reinterpret_cast<const u32x2*>(q);
-            r.v[2 * pc] = w[0];
-            r.v[2 * pc + 1] = w[1];
-          } else {
-            r.v[pc] = *reinterpret_cast<const uint32_t*>(q);
-          }
+      for (int pc = 0; pc < ChunkPages<P>::NV; ++pc) {
+        const uint8_t* q = vbase + (uint64_t)(uint32_t)pg.v[pc] * page_stride + (uint32_t)(d * P);
+        if constexpr (P == 8) {
+          u32x2 w = *reinterpret_cast<const u32x2*>(q);
+          r.v[2 * pc] = w[0];
+          r.v[2 * pc + 1] = w[1];
+        } else {
+          r.v[pc] = *reinterpret_cast<const uint32_t*>(q);
         }
       }
     }
@@ -313,23 +324,36 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
     for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int64_t page_stride = (int64_t)a.n_kv_heads * P * D;
+  const uint32_t page_stride = (uint32_t)a.n_kv_heads * P * D;  // < 2^32: n_kv_heads <= 65535
   const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;
   const uint8_t* vbase = a.v_cache + (int64_t)kvh * P * D;
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
+  const int last = L > 0 ? (L - 1) / P : 0;
 
   // ---- software pipeline over tiles: the QK products of tile it+1 are
   // issued next to the softmax of tile it, so the matrix cores have work
-  // while the vector units run the softmax
+  // while the vector units run the softmax; the bytes of tile it+2 are in
+  // flight meanwhile and the page ids of tile it+3 behind them
   ChunkRegs regs;
+  ChunkPages<P> pg;
   if (ntiles > 0) {
-    chunk_load<D, P>(regs, tid, 0, L, btrow, kbase, vbase, page_stride);
+    chunk_pages<D, P>(pg, tid, 0, last, btrow);
+    chunk_load<D, P>(regs, pg, tid, 0, kbase, vbase, page_stride);
+    if (ntiles > 1) chunk_pages<D, P>(pg, tid, kTile, last, btrow);
     chunk_store<D>(sm, 0, regs, tid, 0, L);
   }
   if (ntiles > 1) {
-    chunk_load<D, P>(regs, tid, kTile, L, btrow, kbase, vbase, page_stride);
+    chunk_load<D, P>(regs, pg, tid, kTile, kbase, vbase, page_stride);
+    if (ntiles > 2) chunk_pages<D, P>(pg, tid, 2 * kTile, last, btrow);
     chunk_store<D>(sm, 1, regs, tid, kTile, L);
   }
+  // Q must have arrived before the loop: otherwise the waits for it that the
+  // compiler places at its first use inside the loop would, on every later
+  // iteration, also wait for the tile loads in flight
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) __asm__ volatile("" ::"v"(qb[nb][c]));
   __syncthreads();
   f32x4 sa[4][kNB], sb[4][kNB];
   u32x4 pk[kNB][2];
@@ -344,7 +368,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
         f32x4 (&nxt)[4][kNB] = half == 0 ? sb : sa;
         const int buf1 = buf == 2 ? 0 : buf + 1;
         const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
-        if (t + 2 < ntiles) chunk_load<D, P>(regs, tid, (t + 2) * kTile, L, btrow, kbase, vbase, page_stride);
+        if (t + 2 < ntiles) {
+          chunk_load<D, P>(regs, pg, tid, (t + 2) * kTile, kbase, vbase, page_stride);
+          if (t + 3 < ntiles) chunk_pages<D, P>(pg, tid, (t + 3) * kTile, last, btrow);
+        }
         if (t + 1 < ntiles) chunk_qk<D>(sm, buf1, n, g, qb, nxt);
         chunk_softmax<D>(cur, t * kTile, g, t * kTile + kTile > wave_lim, lim, a.score_scale, m_run,
                          lacc, o, pk);
