@@ -17,13 +17,15 @@
 // kv-heads as possible, and its L2 holds one head's K/V stream.
 #include "kvfp8_internal.h"
 
+
 namespace kvfp8 {
 namespace {
 
 constexpr int kTile = 64;
 constexpr int kWaves = 8;
 constexpr int kNB = 2;                       // 16-row blocks per wavefront
-constexpr int kRows = kWaves * kNB * 16;     // 256 rows per workgroup
+constexpr int kRows = kWaves * kNB * 16;     // rows per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 
 template <int D>
@@ -43,9 +45,12 @@ __device__ __forceinline__ float wave_max_groups(float x) {
 
 // Raw bytes of one tile held by one thread: 16 K bytes (16 dims of one key) and
 // 16 V bytes (16 keys of one dim).
+template <int D>
 struct ChunkRegs {
-  u32x4 k;
-  u32x4 v;
+  static constexpr int KPT = (kTile * D / 16 + kThreads - 1) / kThreads;  // K segments per thread
+  static constexpr int VPT = (D * 4 + kThreads - 1) / kThreads;           // V segments per thread
+  u32x4 k[KPT];
+  u32x4 v[VPT];
 };
 
 // Page ids of one thread's K row and V keys in one tile, clamped to the
@@ -53,22 +58,30 @@ struct ChunkRegs {
 // fetched one tile ahead of the K/V bytes: the vector memory counter is
 // in-order, and a wait on an id issued just before the bytes of another tile
 // would also wait for those bytes.
-template <int P>
+template <int D, int P>
 struct ChunkPages {
   static constexpr int NV = P >= 16 ? 1 : 16 / P;
-  int32_t k;
-  int32_t v[NV];
+  int32_t k[ChunkRegs<D>::KPT];
+  int32_t v[ChunkRegs<D>::VPT][NV];
 };
 
 template <int D, int P>
-__device__ __forceinline__ void chunk_pages(ChunkPages<P>& pg, int tid, int t0, int last,
+__device__ __forceinline__ void chunk_pages(ChunkPages<D, P>& pg, int tid, int t0, int last,
                                             const int32_t* __restrict__ btrow) {
   constexpr int KSEG = D / 16;  // 16-byte segments per key row
-  if (tid < kTile * KSEG) pg.k = btrow[min((t0 + tid / KSEG) / P, last)];
-  if (tid < D * 4) {
-    const int tv = t0 + 16 * (tid & 3);
 #pragma unroll
-    for (int pc = 0; pc < ChunkPages<P>::NV; ++pc) pg.v[pc] = btrow[min((tv + pc * P) / P, last)];
+  for (int j = 0; j < ChunkRegs<D>::KPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < kTile * KSEG) pg.k[j] = btrow[min((t0 + e / KSEG) / P, last)];
+  }
+#pragma unroll
+  for (int j = 0; j < ChunkRegs<D>::VPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < D * 4) {
+      const int tv = t0 + 16 * (e & 3);
+#pragma unroll
+      for (int pc = 0; pc < ChunkPages<D, P>::NV; ++pc) pg.v[j][pc] = btrow[min((tv + pc * P) / P, last)];
+    }
   }
 }
 
@@ -76,33 +89,41 @@ __device__ __forceinline__ void chunk_pages(ChunkPages<P>& pg, int tid, int t0, 
 // (clamped) last page; their scores are masked and their V bytes cleared in
 // chunk_store.
 template <int D, int P>
-__device__ __forceinline__ void chunk_load(ChunkRegs& r, const ChunkPages<P>& pg, int tid, int t0,
+__device__ __forceinline__ void chunk_load(ChunkRegs<D>& r, const ChunkPages<D, P>& pg, int tid, int t0,
                                            const uint8_t* __restrict__ kbase,
                                            const uint8_t* __restrict__ vbase, uint32_t page_stride) {
   constexpr int KSEG = D / 16;
-  if (tid < kTile * KSEG) {
-    const int kk = tid / KSEG;
-    const int seg = tid % KSEG;
-    const uint32_t off = (uint32_t)(((t0 + kk) % P) * D + 16 * seg);
-    r.k = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(kbase + (uint64_t)(uint32_t)pg.k * page_stride + off));
-  }
-  if (tid < D * 4) {
-    const int d = tid >> 2;
-    const int tv = t0 + 16 * (tid & 3);
-    if constexpr (P >= 16) {
-      r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          vbase + (uint64_t)(uint32_t)pg.v[0] * page_stride + (uint32_t)(d * P + tv % P)));
-    } else {
 #pragma unroll
-      for (int pc = 0; pc < ChunkPages<P>::NV; ++pc) {
-        const uint8_t* q = vbase + (uint64_t)(uint32_t)pg.v[pc] * page_stride + (uint32_t)(d * P);
-        if constexpr (P == 8) {
-          u32x2 w = *reinterpret_cast<const u32x2*>(q);
-          r.v[2 * pc] = w[0];
-          r.v[2 * pc + 1] = w[1];
-        } else {
-          r.v[pc] = *reinterpret_cast<const uint32_t*>(q);
+  for (int j = 0; j < ChunkRegs<D>::KPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < kTile * KSEG) {
+      const int kk = e / KSEG;
+      const int seg = e % KSEG;
+      const uint32_t off = (uint32_t)(((t0 + kk) % P) * D + 16 * seg);
+      r.k[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kbase + (uint64_t)(uint32_t)pg.k[j] * page_stride + off));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < ChunkRegs<D>::VPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < D * 4) {
+      const int d = e >> 2;
+      const int tv = t0 + 16 * (e & 3);
+      if constexpr (P >= 16) {
+        r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            vbase + (uint64_t)(uint32_t)pg.v[j][0] * page_stride + (uint32_t)(d * P + tv % P)));
+      } else {
+#pragma unroll
+        for (int pc = 0; pc < ChunkPages<D, P>::NV; ++pc) {
+          const uint8_t* q = vbase + (uint64_t)(uint32_t)pg.v[j][pc] * page_stride + (uint32_t)(d * P);
+          if constexpr (P == 8) {
+            u32x2 w = *reinterpret_cast<const u32x2*>(q);
+            r.v[j][2 * pc] = w[0];
+            r.v[j][2 * pc + 1] = w[1];
+          } else {
+            r.v[j][pc] = *reinterpret_cast<const uint32_t*>(q);
+          }
         }
       }
     }
@@ -112,37 +133,45 @@ __device__ __forceinline__ void chunk_load(ChunkRegs& r, const ChunkPages<P>& pg
 // Decode the thread's bytes to fp16 and store them in LDS buffer `buf`. Keys at
 // or past the sequence end are stored as zeros (their slots may hold poison).
 template <int D>
-__device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const ChunkRegs& r, int tid, int t0,
+__device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const ChunkRegs<D>& r, int tid, int t0,
                                             int L) {
   constexpr int KSEG = D / 16;
-  if (tid < kTile * KSEG) {
-    const int kk = tid / KSEG;
-    const int seg = tid % KSEG;
-    f16x8 a = e4m3x8_to_f16(r.k[0], r.k[1]);
-    f16x8 b = e4m3x8_to_f16(r.k[2], r.k[3]);
-    // key kk is MFMA row m = 4*(kk/16) + kk%4 of M-tile t = (kk/4)%4; storing it
-    // at LDS row 16t + m makes each QK operand read 16 consecutive rows, which
-    // the padded row stride spreads over distinct banks
-    const int row = 16 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
-    *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg]) = a;
-    *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg + 8]) = b;
-  }
-  if (tid < D * 4) {
-    const int d = tid >> 2;
-    const int kseg = tid & 3;
-    u32x4 w = r.v;
-    const int c = L - (t0 + 16 * kseg);  // valid keys among the 16
-    if (c < 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int cj = c - 4 * j;
-        w[j] &= cj >= 4 ? 0xFFFFFFFFu : (cj <= 0 ? 0u : ((1u << (8 * cj)) - 1u));
-      }
+  for (int j = 0; j < ChunkRegs<D>::KPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < kTile * KSEG) {
+      const int kk = e / KSEG;
+      const int seg = e % KSEG;
+      f16x8 a = e4m3x8_to_f16(r.k[j][0], r.k[j][1]);
+      f16x8 b = e4m3x8_to_f16(r.k[j][2], r.k[j][3]);
+      // key kk is MFMA row m = 4*(kk/16) + kk%4 of M-tile t = (kk/4)%4; storing it
+      // at LDS row 16t + m makes each QK operand read 16 consecutive rows, which
+      // the padded row stride spreads over distinct banks
+      const int row = 16 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
+      *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg]) = a;
+      *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg + 8]) = b;
     }
-    f16x8 a = e4m3x8_to_f16(w[0], w[1]);
-    f16x8 b = e4m3x8_to_f16(w[2], w[3]);
-    *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg]) = a;
-    *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg + 8]) = b;
+  }
+#pragma unroll
+  for (int j = 0; j < ChunkRegs<D>::VPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < D * 4) {
+      const int d = e >> 2;
+      const int kseg = e & 3;
+      u32x4 w = r.v[j];
+      const int c = L - (t0 + 16 * kseg);  // valid keys among the 16
+      if (c < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ci = c - 4 * i;
+          w[i] &= ci >= 4 ? 0xFFFFFFFFu : (ci <= 0 ? 0u : ((1u << (8 * ci)) - 1u));
+        }
+      }
+      f16x8 a = e4m3x8_to_f16(w[0], w[1]);
+      f16x8 b = e4m3x8_to_f16(w[2], w[3]);
+      *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg]) = a;
+      *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg + 8]) = b;
+    }
   }
 }
 
@@ -251,7 +280,7 @@ __device__ __forceinline__ void chunk_pv(const ChunkLds<D>& sm, int buf, int n, 
 }
 
 template <int D, int P>
-__global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attn_chunk_kernel(const AttnArgs a) {
   constexpr int NC = D / 32;
   constexpr int NBLK = D / 16;
   __shared__ __attribute__((aligned(16))) ChunkLds<D> sm;
@@ -334,8 +363,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_chunk_kernel(const AttnAr
   // issued next to the softmax of tile it, so the matrix cores have work
   // while the vector units run the softmax; the bytes of tile it+2 are in
   // flight meanwhile and the page ids of tile it+3 behind them
-  ChunkRegs regs;
-  ChunkPages<P> pg;
+  ChunkRegs<D> regs;
+  ChunkPages<D, P> pg;
   if (ntiles > 0) {
     chunk_pages<D, P>(pg, tid, 0, last, btrow);
     chunk_load<D, P>(regs, pg, tid, 0, kbase, vbase, page_stride);
