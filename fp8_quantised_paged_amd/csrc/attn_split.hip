@@ -145,6 +145,65 @@ __device__ __forceinline__ void load_tile(TileRegs<D, P>& r, const PageRegs<P>& 
   }
 }
 
+// Bytes of one tile per wavefront (K and V codes): the LDS staging area of the
+// verify pipeline.
+template <int D>
+constexpr int kTileBytes = 2 * kTile * D;
+
+// The same 16-byte loads as load_tile (P >= 16), issued as direct-to-LDS
+// loads: load i writes each lane's 16 bytes at lds + 1024 i + 16 lane, so the
+// tile occupies no registers while in flight. The caller waits for the
+// vector memory counter before read_tile_lds.
+template <int D, int P>
+__device__ __forceinline__ void load_tile_lds(uint8_t* lds, const PageRegs<P>& pr, const LaneOffsets<D, P>& lo,
+                                              const uint8_t* __restrict__ kbase,
+                                              const uint8_t* __restrict__ vbase, uint32_t page_stride) {
+  static_assert(P >= 16, "V bytes of one dimension must be 16 contiguous bytes");
+  constexpr int KD = D / 16;
+  // both page addresses first: no page-id register is read once loads of this
+  // tile are in flight
+  const uint8_t* kp = kbase + (uint64_t)(uint32_t)pr.k[0] * page_stride;
+  const uint8_t* vp = vbase + (uint64_t)(uint32_t)pr.v[0] * page_stride + lo.v;
+  __asm__ volatile("" ::"v"(kp), "v"(vp));
+  int i = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < KD / 4; ++j, ++i)
+      __builtin_amdgcn_global_load_lds(kp + lo.k[t] + 64 * j, (__attribute__((address_space(3))) void*)(lds + 1024 * i),
+                                       16, 0, 0);
+#pragma unroll
+  for (int blk = 0; blk < D / 16; ++blk, ++i)
+    __builtin_amdgcn_global_load_lds(vp + blk * 16 * P, (__attribute__((address_space(3))) void*)(lds + 1024 * i), 16,
+                                     0, 0);
+}
+
+// Each lane reads back its own 16-byte pieces (conflict-free: consecutive
+// lanes, consecutive 16 bytes) into the register tile.
+template <int D, int P>
+__device__ __forceinline__ void read_tile_lds(TileRegs<D, P>& r, const uint8_t* lds, int lane) {
+  constexpr int KD = D / 16;
+  int i = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < KD / 4; ++j, ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(lds + 1024 * i + 16 * lane);
+      r.k[t][4 * j + 0] = w[0];
+      r.k[t][4 * j + 1] = w[1];
+      r.k[t][4 * j + 2] = w[2];
+      r.k[t][4 * j + 3] = w[3];
+    }
+#pragma unroll
+  for (int blk = 0; blk < D / 16; ++blk, ++i) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(lds + 1024 * i + 16 * lane);
+    r.v[blk][0] = w[0];
+    r.v[blk][1] = w[1];
+    r.v[blk][2] = w[2];
+    r.v[blk][3] = w[3];
+  }
+}
+
 // Rows keep a reference maximum m_ref for their probabilities and rescale
 // their accumulators only when some row's maximum moves more than kLazy (log2
 // units) above it: probabilities are then at most 2^kLazy, which fp16 and the
@@ -153,9 +212,10 @@ __device__ __forceinline__ void load_tile(TileRegs<D, P>& r, const PageRegs<P>& 
 // the end.
 constexpr float kLazy = 8.0f;
 
-template <int D, int P, int NB>
+template <int D, int P, int NB, bool QREG>
 __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, int g,
-                                             const f16x8 (*sq)[D / 32][64], const int (&lim)[NB],
+                                             const f16x8 (*sq)[D / 32][64], const f16x8 (&qreg)[NB][D / 32],
+                                             const int (&lim)[NB],
                                              float score_scale, float (&m_ref)[NB], float (&m_max)[NB],
                                              float (&l_run)[NB], f32x4 (&o)[NB][D / 16]) {
   constexpr int NBLK = D / 16;
@@ -170,9 +230,9 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
       for (int blk = 0; blk < NBLK; ++blk) r.v[blk][w4] &= mask;
     }
   }
-  // ---- S^T = K Q^T. Q is re-read from LDS every tile (the empty asm keeps
-  // the compiler from hoisting it into registers, which the K/V double buffer
-  // needs).
+  // ---- S^T = K Q^T. Q is in registers (QREG) or re-read from LDS every tile
+  // (the empty asm keeps the compiler from hoisting it into registers, which
+  // the K/V double buffer needs).
   __asm__ volatile("" ::: "memory");
   const int lane = threadIdx.x & 63;
   f32x4 sc[4][NB];
@@ -184,7 +244,12 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
   for (int c = 0; c < D / 32; ++c) {
     f16x8 qop[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) qop[nb] = sq[nb][c][lane];
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (QREG)
+        qop[nb] = qreg[nb][c];
+      else
+        qop[nb] = sq[nb][c][lane];
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f16x8 ka = e4m3x8_to_f16(r.k[t][2 * c], r.k[t][2 * c + 1]);
@@ -298,9 +363,12 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int32_t* btrow = a.block_table + (int64_t)b * a.max_pages;
   const int last = L > 0 ? (L - 1) / P : 0;
 
-  // ---- start-up: wavefront 0 loads the Q rows while every wavefront loads
-  // its first page ids, then the first tile's K/V are issued before Q goes to
-  // LDS, so the three latencies overlap instead of adding up.
+  // ---- start-up: the Q rows and the first page ids load together; Q goes to
+  // LDS before the first tile's K/V are issued, so the latencies overlap
+  // instead of adding up. Every wavefront loads Q (a few KB, cache hits) and
+  // wavefront 0 stores it: with the loads in a wave-uniform branch the
+  // compiler could no longer count them exactly, and its wait before reusing
+  // their registers would also wait for the tile in flight.
   // Q operand: dims g*D/4 + 8c + i of row n of each 16-row block.
   f16x8 qraw[NB][NC];
   int lim[NB];
@@ -309,34 +377,40 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
     const int rr = nb * 16 + n;
     const int i = rr / G;
     lim[nb] = rr < nrows ? min(end, L - T + i + 1) : 0;
-    if (wave == 0) {
-      if (rr < nrows) {
-        const int h = kvh * G + rr % G;
-        const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
+    if (rr < nrows) {
+      const int h = kvh * G + rr % G;
+      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          qraw[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
-      } else {
+      for (int c = 0; c < NC; ++c)
+        qraw[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
+    } else {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) qraw[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      for (int c = 0; c < NC; ++c) qraw[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   int it = wave;
   PageRegs<P> pa, pb;
   TileRegs<D, P> ra;
-  if (it < ntiles) {
-    load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
-    if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-    load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
-  }
+  // Page ids are loaded unconditionally (they are clamped to the sequence's
+  // last page, and every block-table row has an entry): a load on only one
+  // side of a branch would make the compiler's wait counts inexact.
+  load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+  load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
   if (wave == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int c = 0; c < NC; ++c) sm_q[nb][c][lane] = qraw[nb][c];
   }
-  __syncthreads();
+  // The tile bytes are issued only after Q is in LDS (the vector memory
+  // counter is in-order: a wait for Q issued behind them would wait for
+  // them), and the barrier waits for LDS only, so they stay in flight
+  // across it (a full __syncthreads would also wait for every vector load).
+  // the verify pipeline stages every tile, the first included, through LDS
+  constexpr bool kStaged = NB == 2 && P >= 16;
+  __asm__ volatile("" ::: "memory");
+  if (!kStaged && it < ntiles) load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   float m_ref[NB], m_max[NB], l_run[NB];
   f32x4 o[NB][NBLK];
@@ -351,30 +425,59 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
 
   // ---- tiles. With one 16-row block (decode) two register buffers keep the
   // next tile's K/V in flight while the current one is computed, and page ids
-  // are fetched two tiles ahead; with two blocks (verify) the accumulators
-  // leave room for one buffer only, and the second wavefront per SIMD covers
-  // the latency instead.
+  // are fetched two tiles ahead.
   if constexpr (NB == 1) {
     if (it < ntiles) {
       TileRegs<D, P> rb;
       while (true) {
-        if (it + 2 * W < ntiles) load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
+        load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
         if (it + W < ntiles) load_tile<D, P>(rb, pb, lo, kbase, vbase, page_stride);
-        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_tile<D, P, NB, false>(ra, start + it * kTile, L, g, sm_q, qraw, lim, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
-        if (it + 2 * W < ntiles) load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
+        load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
         if (it + W < ntiles) load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
-        compute_tile<D, P, NB>(rb, start + it * kTile, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_tile<D, P, NB, false>(rb, start + it * kTile, L, g, sm_q, qraw, lim, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
       }
     }
+  } else if constexpr (kStaged) {
+    // With two blocks (verify) the accumulators leave room for one register
+    // tile; the next tile streams into this wavefront's part of the merge
+    // area (unused until the merge) with direct-to-LDS loads, and Q stays in
+    // registers (reading it from LDS would make the compiler wait for the
+    // staged loads, which it cannot tell apart from Q).
+    static_assert(W * kTileBytes<D> <= (int)sizeof(sm_o), "tile staging must fit in the merge area");
+    uint8_t* tb = reinterpret_cast<uint8_t*>(&sm_o[0][0][0]) + wave * kTileBytes<D>;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) __asm__ volatile("" ::"v"(qraw[nb][c]));  // Q complete before the loop
+    if (it < ntiles) {
+      load_tile_lds<D, P>(tb, pa, lo, kbase, vbase, page_stride);
+      __builtin_amdgcn_s_waitcnt(0);
+      read_tile_lds<D, P>(ra, tb, lane);
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (it + W < ntiles) load_tile_lds<D, P>(tb, pb, lo, kbase, vbase, page_stride);
+      while (true) {
+        load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
+        compute_tile<D, P, NB, true>(ra, start + it * kTile, L, g, nullptr, qraw, lim, a.score_scale, m_ref, m_max, l_run,
+                               o);
+        it += W;
+        if (it >= ntiles) break;
+        __builtin_amdgcn_s_waitcnt(0);  // the staged tile (and the page ids) have landed
+        read_tile_lds<D, P>(ra, tb, lane);
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before it is overwritten
+        if (it + W < ntiles) load_tile_lds<D, P>(tb, pb, lo, kbase, vbase, page_stride);
+      }
+    }
+    __syncthreads();  // every wavefront is done with its staging area before the merge
   } else {
     if (it < ntiles) {
       while (true) {
-        if (it + W < ntiles) load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-        compute_tile<D, P, NB>(ra, start + it * kTile, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
+        load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+        compute_tile<D, P, NB, false>(ra, start + it * kTile, L, g, sm_q, qraw, lim, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
         load_tile<D, P>(ra, pb, lo, kbase, vbase, page_stride);
