@@ -118,6 +118,7 @@ kvfp8::AttnArgs make_args(const AttnCommon& c, const int32_t* cu_q, int64_t n_ro
   a.max_q_len = max_q;
   a.score_scale = c.k_scale * c.sm_scale * kvfp8::kLog2e;
   a.v_scale = c.v_scale;
+  a.k_scale = c.k_scale;
   if (c.num_splits > 1) {
     float* ws = c.workspace;
     int64_t units = n_rows * c.n_q_heads * (int64_t)c.num_splits;
@@ -131,12 +132,25 @@ kvfp8::AttnArgs make_args(const AttnCommon& c, const int32_t* cu_q, int64_t n_ro
   return a;
 }
 
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+};
+
 int32_t run_attention(const AttnCommon& c, const int32_t* cu_q, int64_t n_rows, int32_t max_q,
-                      hipStream_t stream) {
+                      hipStream_t stream, const AppendArgs* app = nullptr) {
   if (c.batch == 0 || n_rows == 0) return ok();
   const int32_t group = c.n_q_heads / c.n_kv_heads;
   const int64_t rows = (int64_t)max_q * group;
   kvfp8::AttnArgs a = make_args(c, cu_q, n_rows, max_q);
+  if (app) {
+    a.k_new = app->k_new;
+    a.v_new = app->v_new;
+    a.k_cache_w = app->k_cache;
+    a.v_cache_w = app->v_cache;
+  }
   hipError_t e;
   if (rows <= kSplitRows) {
     e = kvfp8::launch_attn_split(a, (int)rows, stream);
@@ -251,6 +265,30 @@ KVFP8_API int32_t paged_attn_e4m3_decode(const uint16_t* q_f16, const uint8_t* k
     return fail(KVFP8_UNSUPPORTED, "GQA group of %d heads (at most %d)", n_q_heads / n_kv_heads,
                 kSplitRows);
   return run_attention(c, nullptr, batch, 1, stream);
+}
+
+KVFP8_API int32_t paged_attn_e4m3_decode_append(const uint16_t* q_f16, const uint16_t* k_new,
+                                                const uint16_t* v_new, uint8_t* k_cache, uint8_t* v_cache,
+                                                const int32_t* block_table, const int32_t* seq_lens,
+                                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                                int32_t head_dim, int32_t page_size,
+                                                int32_t max_pages_per_seq, float k_scale, float v_scale,
+                                                float sm_scale, int32_t num_splits, float* workspace,
+                                                size_t workspace_bytes, uint16_t* out_f16,
+                                                hipStream_t stream) {
+  AttnCommon c{q_f16, k_cache, v_cache, block_table, seq_lens, batch, n_q_heads, n_kv_heads,
+               head_dim, page_size, max_pages_per_seq, k_scale, v_scale, sm_scale, num_splits,
+               workspace, workspace_bytes, out_f16};
+  int32_t st = check_common(c, batch);
+  if (st != KVFP8_OK) return st;
+  if (n_q_heads / n_kv_heads > kSplitRows)
+    return fail(KVFP8_UNSUPPORTED, "GQA group of %d heads (at most %d)", n_q_heads / n_kv_heads,
+                kSplitRows);
+  if (batch > 0 && (!k_new || !v_new)) return fail(KVFP8_INVALID_ARG, "null new-token pointer");
+  if (batch > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(KVFP8_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  const AppendArgs app{k_new, v_new, k_cache, v_cache};
+  return run_attention(c, nullptr, batch, 1, stream, &app);
 }
 
 KVFP8_API int32_t paged_attn_e4m3_verify(const uint16_t* q_f16, const int32_t* cu_q_lens,

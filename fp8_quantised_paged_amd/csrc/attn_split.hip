@@ -356,6 +356,30 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int end = min(start + chunk, L);
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
 
+  // ---- append (decode only): the wavefront that will load the tile holding
+  // key L - 1 first quantises the sequence's new token into that slot, exactly
+  // as the cache write does, and waits for its stores before any load of its
+  // own; no other wavefront or workgroup reads that page.
+  if constexpr (NB == 1) {
+    if (a.k_new != nullptr && ntiles > 0 && end == L && wave == (ntiles - 1) % W) {
+      constexpr int PER = D / 64;  // dims per lane
+      const int pos = L - 1;
+      const uint64_t page = (uint32_t)a.block_table[(int64_t)b * a.max_pages + pos / P];
+      const int off = pos % P;
+      const int64_t src = ((int64_t)b * a.n_kv_heads + kvh) * D + PER * lane;
+      uint8_t* kd = a.k_cache_w + ((page * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
+      uint8_t* vd = a.v_cache_w + ((page * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const float kx = (float)__builtin_bit_cast(_Float16, a.k_new[src + j]);
+        const float vx = (float)__builtin_bit_cast(_Float16, a.v_new[src + j]);
+        kd[j] = (uint8_t)e4m3_encode(kx / a.k_scale);
+        vd[(int64_t)j * P] = (uint8_t)e4m3_encode(vx / a.v_scale);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
+
   const uint32_t page_stride = (uint32_t)a.n_kv_heads * P * D;  // < 2^32: n_kv_heads <= 65535
   const LaneOffsets<D, P> lo(n, g);
   const uint8_t* kbase = a.k_cache + (int64_t)kvh * P * D;

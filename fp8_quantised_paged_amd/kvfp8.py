@@ -24,6 +24,7 @@ EXPORTED = (
     "kv_calibrate_amax",
     "kv_quant_write",
     "paged_attn_e4m3_decode",
+    "paged_attn_e4m3_decode_append",
     "paged_attn_e4m3_verify",
     "split_reduce_fp32",
     "kvfp8_attn_workspace_bytes",
@@ -54,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "kv_quant_write": (I32, [P, P, P, I64, I32, I32, I32, I64, F32, F32, P, P, P]),
         "paged_attn_e4m3_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, F32, F32,
                                          I32, P, SZ, P, P]),
+        "paged_attn_e4m3_decode_append": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32,
+                                                F32, F32, I32, P, SZ, P, P]),
         "paged_attn_e4m3_verify": (I32, [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                          F32, F32, F32, I32, P, SZ, P, P]),
         "split_reduce_fp32": (I32, [P, P, P, I32, I32, I32, I32, P, P, P]),
@@ -230,6 +233,41 @@ def paged_attn_e4m3_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                        block_table.shape[1], float(k_scale), float(v_scale),
                                        float(sm_scale), int(num_splits), ws_ptr, ws_bytes, _ptr(out),
                                        _stream()), "paged_attn_e4m3_decode")
+    return out
+
+
+def paged_attn_e4m3_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                                  seq_lens: torch.Tensor, k_scale: float, v_scale: float, sm_scale: float,
+                                  num_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                                  out: Optional[torch.Tensor] = None, partials_only: bool = False
+                                  ) -> Optional[torch.Tensor]:
+    """Decode with each sequence's new token appended: k_new, v_new fp16 [B, Hkv, D] are quantised
+    into key position seq_lens[b] - 1 (located through the block table), then attended.
+    Returns out fp16 [B, Hq, D] (None with partials_only)."""
+    _need(q, "q", torch.float16, 3)
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, hq, d = q.shape
+    hkv, psz, _ = _cache_dims(k_cache, v_cache, d)
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{B}, {hkv}, {d}]")
+    if partials_only:
+        out = None
+    elif out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16, 3)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.paged_attn_e4m3_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                              k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                              seq_lens.data_ptr(), B, hq, hkv, d, psz, block_table.shape[1],
+                                              float(k_scale), float(v_scale), float(sm_scale), int(num_splits),
+                                              ws_ptr, ws_bytes, _ptr(out), _stream()),
+           "paged_attn_e4m3_decode_append")
     return out
 
 

@@ -134,6 +134,26 @@ int32_t paged_attn_e4m3_decode(const uint16_t* q_f16, const uint8_t* k_cache, co
                                float v_scale, float sm_scale, int32_t num_splits, float* workspace,
                                size_t workspace_bytes, uint16_t* out_f16, hipStream_t stream);
 
+/* Decode step with the new token appended ([P2] Changes: the quantising cache
+ * write and the decode route over the E4M3 cache, one step). For every
+ * sequence b with L = seq_lens[b] >= 1, the new token's K and V (k_new, v_new:
+ * [batch][n_kv_heads][head_dim] fp16, 16-byte aligned) are quantised exactly
+ * as kv_quant_write does (same scales, same rounding and saturation) into key
+ * position L - 1, i.e. slot block_table[b][(L-1)/page_size] * page_size +
+ * (L-1) % page_size; then attention runs as paged_attn_e4m3_decode over keys
+ * 0 .. L-1, the new one included. seq_lens counts the new token. The result
+ * (cache bytes and output) equals kv_quant_write with those slots followed by
+ * paged_attn_e4m3_decode. k_cache and v_cache are written (the new tokens'
+ * bytes only). Other arguments, errors and the workspace as for
+ * paged_attn_e4m3_decode. */
+int32_t paged_attn_e4m3_decode_append(const uint16_t* q_f16, const uint16_t* k_new, const uint16_t* v_new,
+                                      uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                      int32_t max_pages_per_seq, float k_scale, float v_scale, float sm_scale,
+                                      int32_t num_splits, float* workspace, size_t workspace_bytes,
+                                      uint16_t* out_f16, hipStream_t stream);
+
 /* Multi-query attention with a causal mask among each sequence's query tokens:
  * MTP verify of 1 + drafted tokens ([P1] Purpose and Validation on 4xV100 TP4:
  * MTP3 verifies up to four tokens per step) and prefill/catch-up chunks in mixed

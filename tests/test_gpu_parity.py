@@ -188,11 +188,51 @@ def test_decode_parity(K, case, S):
     assert_close_attn(out, ref, f"{case} S={S}")
 
 
+APPEND_CASES = {
+    # new tokens at a page start, mid-page, the first key, and a tile edge
+    "d128_p16": lambda: make_batch([1, 16, 17, 64, 65, 300], [1] * 6, 32, 4, 128, 16, seed=57),
+    "d64_p8": lambda: make_batch([9, 130, 8], [1] * 3, 16, 4, 64, 8, seed=58),
+    "d128_p64_g4": lambda: make_batch([700, 64, 129], [1] * 3, 16, 4, 128, 64, seed=59),
+}
+
+
+@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("case", list(APPEND_CASES))
+def test_decode_append_equals_write_then_decode(K, case, S):
+    """The fused step writes exactly the bytes kv_quant_write would (every cache
+    byte against the oracle) and returns the separate write-then-decode result
+    bit for bit."""
+    bt = APPEND_CASES[case]()
+    _, sc = oracle_scales(bt)
+    ks, vs, sm = float(sc[0]), float(sc[1]), float(sm_of(bt))
+    db = DeviceBatch(bt)
+    prior, new = dev(bt.prior_rows()), dev(bt.new_token_rows())
+    K.kv_quant_write(db.k[prior].contiguous(), db.v[prior].contiguous(), db.slots[prior].contiguous(), ks, vs,
+                     db.k_cache, db.v_cache)
+    kc_sep, vc_sep = db.k_cache.clone(), db.v_cache.clone()
+    k_new, v_new = db.k[new].contiguous(), db.v[new].contiguous()
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
+    out = K.paged_attn_e4m3_decode_append(db.q, k_new, v_new, db.k_cache, db.v_cache, db.block_table,
+                                          db.seq_lens, ks, vs, sm, num_splits=S, workspace=ws).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    assert np.array_equal(db.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy(), vc)
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm_of(bt))
+    assert_close_attn(out, ref, f"append {case} S={S}")
+    K.kv_quant_write(k_new, v_new, db.slots[new].contiguous(), ks, vs, kc_sep, vc_sep)
+    sep = K.paged_attn_e4m3_decode(db.q, kc_sep, vc_sep, db.block_table, db.seq_lens, ks, vs, sm, num_splits=S,
+                                   workspace=ws).cpu().numpy()
+    assert np.array_equal(out.view(np.uint16), sep.view(np.uint16))
+
+
 VERIFY_CASES = {
     "mtp3_small": lambda: make_batch([1024, 70, 4, 300], [4] * 4, 32, 4, 128, 16, seed=61),
     "ragged_q": lambda: make_batch([50, 9, 200, 3], [1, 2, 4, 3], 32, 4, 128, 16, seed=62),
     "d64_p4": lambda: make_batch([100, 257], [4, 2], 8, 2, 64, 4, seed=63),
     "g4_q8": lambda: make_batch([129, 64], [8, 5], 16, 4, 64, 16, seed=64),
+    # 32 rows per kv-head with pages of 32 and 64 keys: the LDS-staged verify pipeline
+    "p64_q4": lambda: make_batch([700, 64, 129], [4, 2, 3], 32, 4, 128, 64, seed=65),
+    "p32_g16_q2": lambda: make_batch([300, 41, 5], [2, 2, 1], 32, 2, 128, 32, seed=66),
 }
 
 
