@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvfp8.so")
-SOURCES = ["api.cpp", "calibrate.hip", "quant_write.hip", "attn_split.hip", "attn_chunk.hip",
-           "split_reduce.hip"]
+SOURCES = ["api.cpp", "scale_overlay.cpp", "calibrate.hip", "quant_write.hip", "attn_split.hip",
+           "attn_chunk.hip", "split_reduce.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -31,6 +31,15 @@ int32_t ok() {
   return KVFP8_OK;
 }
 
+}  // namespace
+
+namespace kvfp8 {
+void set_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+void clear_error() { g_err[0] = '\0'; }
+}  // namespace kvfp8
+
+namespace {
+
 int32_t hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(KVFP8_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));

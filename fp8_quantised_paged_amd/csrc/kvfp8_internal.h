@@ -83,6 +83,10 @@ struct AttnArgs {
   float k_scale;
 };
 
+// the library's thread-local error text (kvfp8_last_error)
+void set_error(const char* msg);
+void clear_error();
+
 hipError_t launch_calibrate(const uint16_t* x, int64_t n_tensors, int64_t n_elems, float* amax,
                             float* scale, hipStream_t stream);
 hipError_t launch_quant_write(const uint16_t* k, const uint16_t* v, const int64_t* slots,

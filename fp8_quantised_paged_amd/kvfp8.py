@@ -32,6 +32,8 @@ EXPORTED = (
     "kvfp8_last_error",
     "kvfp8_e4m3_encode_f32",
     "kvfp8_e4m3_decode_f32",
+    "kvfp8_scale_overlay_write",
+    "kvfp8_scale_overlay_read",
 )
 
 
@@ -62,6 +64,8 @@ def _load() -> ctypes.CDLL:
         "split_reduce_fp32": (I32, [P, P, P, I32, I32, I32, I32, P, P, P]),
         "kvfp8_e4m3_encode_f32": (I32, [P, P, I64, P]),
         "kvfp8_e4m3_decode_f32": (I32, [P, P, I64, P]),
+        "kvfp8_scale_overlay_write": (I32, [ctypes.c_char_p, ctypes.c_char_p, I32, P, P]),
+        "kvfp8_scale_overlay_read": (I32, [ctypes.c_char_p, ctypes.c_char_p, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -335,3 +339,25 @@ def kvfp8_e4m3_decode_f32(codes: torch.Tensor) -> torch.Tensor:
     _check(_lib.kvfp8_e4m3_decode_f32(codes.data_ptr(), x.data_ptr(), codes.numel(), _stream()),
            "kvfp8_e4m3_decode_f32")
     return x
+
+
+def scale_overlay_write(path: str, revision: str, k_scales, v_scales) -> None:
+    """Store per-layer K/V scales (host sequences of fp32) for a checkpoint revision."""
+    import numpy as np
+    k = np.ascontiguousarray(np.asarray(k_scales, dtype=np.float32))
+    v = np.ascontiguousarray(np.asarray(v_scales, dtype=np.float32))
+    if k.ndim != 1 or k.shape != v.shape:
+        raise ValueError("k_scales and v_scales must be 1-D of equal length")
+    _check(_lib.kvfp8_scale_overlay_write(os.fsencode(path), revision.encode(), int(k.size),
+                                          k.ctypes.data, v.ctypes.data), "kvfp8_scale_overlay_write")
+
+
+def scale_overlay_read(path: str, revision: str, n_layers: int):
+    """Per-layer (k_scales, v_scales) fp32 arrays for `revision`; raises KVFP8Error on anything
+    missing, foreign or invalid (no fallback)."""
+    import numpy as np
+    k = np.zeros(int(n_layers), np.float32)
+    v = np.zeros(int(n_layers), np.float32)
+    _check(_lib.kvfp8_scale_overlay_read(os.fsencode(path), revision.encode(), int(n_layers), k.ctypes.data,
+                                         v.ctypes.data), "kvfp8_scale_overlay_read")
+    return k, v

@@ -194,6 +194,26 @@ int32_t split_reduce_fp32(const float* ws_o, const float* ws_m, const float* ws_
 int32_t kvfp8_e4m3_encode_f32(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 int32_t kvfp8_e4m3_decode_f32(const uint8_t* codes, float* x, int64_t n, hipStream_t stream);
 
+/* Revision-bound per-layer scale file ([P2] Changes: the E4M3 mode requires
+ * every per-layer K/V scale, finite and positive, and refuses to start when the
+ * calibrated overlay is missing or incomplete; [P2] Validation boundary: the
+ * overlay must have been generated for the exact checkpoint revision, with no
+ * generic or unit-scale fallback). Host-only; all pointers are host pointers.
+ * kvfp8_scale_overlay_write stores n_layers (k_scale, v_scale) pairs for
+ * `revision` (1..255 printable characters, no whitespace) at `path` (written to
+ * path.tmp, then renamed); the scales are written as hexadecimal floats, so
+ * reading returns them bit for bit. It refuses a scale that is not finite,
+ * positive and normal (KVFP8_BAD_SCALE).
+ * kvfp8_scale_overlay_read fails closed: a missing or malformed file, another
+ * revision, another layer count, a layer missing or given twice
+ * (KVFP8_INVALID_ARG) or an invalid scale (KVFP8_BAD_SCALE) returns an error and
+ * leaves k_scales and v_scales untouched; on success both are filled
+ * ([n_layers] fp32, layer order). */
+int32_t kvfp8_scale_overlay_write(const char* path, const char* revision, int32_t n_layers, const float* k_scales,
+                                  const float* v_scales);
+int32_t kvfp8_scale_overlay_read(const char* path, const char* revision, int32_t n_layers, float* k_scales,
+                                 float* v_scales);
+
 #ifdef __cplusplus
 }
 #endif
