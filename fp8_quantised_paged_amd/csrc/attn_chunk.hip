@@ -17,6 +17,8 @@
 // kv-heads as possible, and its L2 holds one head's K/V stream.
 #include "kvfp8_internal.h"
 
+#include <type_traits>
+
 
 namespace kvfp8 {
 namespace {
@@ -195,39 +197,47 @@ __device__ __forceinline__ void chunk_qk(const ChunkLds<D>& sm, int buf, int n, 
 }
 
 // Online softmax of one tile (log2 units; the positive scale is applied to
-// the raw max and folded into the exponent's FMA). Produces the fp16
-// probabilities packed as the PV B operand and rescales o / lacc when a row
-// max moved.
-template <int D>
-__device__ __forceinline__ void chunk_softmax(f32x4 (&sc)[4][kNB], int t0, int g, bool masked,
-                                              const int (&lim)[kNB], float score_scale,
-                                              float (&m_run)[kNB], f32x4 (&lacc)[kNB],
-                                              f32x4 (&o)[kNB][D / 16], u32x4 (&pk)[kNB][2]) {
+// the raw max and folded into the exponent's FMA). A row keeps a reference
+// maximum m_ref for its probabilities and moves it (rescaling o and l) only
+// when some row's maximum grows more than kLazy above its reference: the
+// probabilities are then at most 2^kLazy, which fp16 and the fp32 sums hold as
+// well as values below 1, and after the first tiles the rescale almost never
+// runs. The new reference is chosen without a branch, so the maxima and the
+// probabilities are straight-line code the scheduler can interleave with the
+// next tile's QK products; only the rescale multiplies sit behind a
+// (wave-uniform, rare) branch. m_max tracks the true maximum; the state is
+// brought to it at the end. MASKED selects out keys at or past a row's limit.
+constexpr float kLazy = 8.0f;
+
+template <int D, bool MASKED>
+__device__ __forceinline__ void chunk_softmax(f32x4 (&sc)[4][kNB], int t0, int g, const int (&lim)[kNB],
+                                              float score_scale, float (&m_ref)[kNB], float (&m_max)[kNB],
+                                              f32x4 (&lacc)[kNB], f32x4 (&o)[kNB][D / 16],
+                                              u32x4 (&pk)[kNB][2]) {
   constexpr int NBLK = D / 16;
-  float mnew[kNB], mold[kNB];
+  float alpha[kNB];
+  bool moved[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    float tmax = -INFINITY;
-    if (masked) {
+    if constexpr (MASKED) {
+      const int rem = lim[nb] - t0 - 16 * g;  // keys 16g + k of the tile with k < rem are visible
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = t0 + 16 * g + 4 * t + i;
-          const float v = tok < lim[nb] ? sc[t][nb][i] : -INFINITY;
-          sc[t][nb][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][nb][i]);
+        for (int i = 0; i < 4; ++i)
+          if (4 * t + i >= rem) sc[t][nb][i] = -INFINITY;
     }
-    tmax = wave_max_groups(tmax) * score_scale;
-    mold[nb] = m_run[nb];
-    mnew[nb] = fmaxf(mold[nb], tmax);
-    const float mref = (mnew[nb] == -INFINITY) ? 0.0f : mnew[nb];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][nb][i]);
+    m_max[nb] = fmaxf(m_max[nb], wave_max_groups(tmax) * score_scale);
+    moved[nb] = __builtin_amdgcn_ballot_w64(m_max[nb] > m_ref[nb] + kLazy) != 0;
+    const float m_new = moved[nb] ? m_max[nb] : m_ref[nb];
+    alpha[nb] = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+    m_ref[nb] = m_new;
+    const float nref = (m_new == -INFINITY) ? 0.0f : -m_new;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -235,21 +245,19 @@ __device__ __forceinline__ void chunk_softmax(f32x4 (&sc)[4][kNB], int t0, int g
         const int t = 2 * u + (j >> 1);
         const int i = 2 * (j & 1);
         f32x2 pp;
-        pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i], score_scale, -mref));
-        pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i + 1], score_scale, -mref));
+        pp[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i], score_scale, nref));
+        pp[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][nb][i + 1], score_scale, nref));
         pk[nb][u][j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, f16x2));
       }
     }
   }
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    if (__builtin_amdgcn_ballot_w64(mnew[nb] != mold[nb]) != 0) {
-      const float alpha = (mnew[nb] == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[nb] - mnew[nb]);
-      lacc[nb] *= alpha;
+    if (moved[nb]) {
+      lacc[nb] *= alpha[nb];
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha;
+      for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= alpha[nb];
     }
-    m_run[nb] = mnew[nb];
   }
 }
 
@@ -342,12 +350,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_chunk_kernel(const AttnArgs 
     wave_lim = first < nrows ? L - T + first / G + 1 : 0;
   }
 
-  float m_run[kNB];
+  float m_ref[kNB], m_max[kNB];
   f32x4 lacc[kNB];  // row sums of P, accumulated on the matrix core (A = ones)
   f32x4 o[kNB][NBLK];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    m_run[nb] = -INFINITY;
+    m_ref[nb] = -INFINITY;
+    m_max[nb] = -INFINITY;
     lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -388,6 +397,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_chunk_kernel(const AttnArgs 
   u32x4 pk[kNB][2];
   if (ntiles > 0) chunk_qk<D>(sm, 0, n, g, qb, sa);
   int buf = 0;  // buffer of tile it
+  // Loop body without data-dependent branches in the common case: the loads
+  // of tiles t+2 / page ids of t+3, the next tile's QK and the stores run even
+  // past the last tile (clamped pages, buffers no one reads afterwards), so the
+  // QK products and the softmax form one block the scheduler can interleave.
+  auto body = [&](auto masked_tag, int t, f32x4 (&cur)[4][kNB], f32x4 (&nxt)[4][kNB]) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int buf1 = buf == 2 ? 0 : buf + 1;
+    const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
+    chunk_load<D, P>(regs, pg, tid, (t + 2) * kTile, kbase, vbase, page_stride);
+    chunk_pages<D, P>(pg, tid, (t + 3) * kTile, last, btrow);
+    chunk_qk<D>(sm, buf1, n, g, qb, nxt);
+    chunk_softmax<D, MASKED>(cur, t * kTile, g, lim, a.score_scale, m_ref, m_max, lacc, o, pk);
+    chunk_pv<D>(sm, buf, n, g, pk, lacc, o);
+    chunk_store<D>(sm, buf2, regs, tid, (t + 2) * kTile, L);
+    __syncthreads();
+    buf = buf1;
+  };
   for (int it = 0; it < ntiles; it += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -395,21 +421,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_chunk_kernel(const AttnArgs 
       if (t < ntiles) {
         f32x4 (&cur)[4][kNB] = half == 0 ? sa : sb;
         f32x4 (&nxt)[4][kNB] = half == 0 ? sb : sa;
-        const int buf1 = buf == 2 ? 0 : buf + 1;
-        const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
-        if (t + 2 < ntiles) {
-          chunk_load<D, P>(regs, pg, tid, (t + 2) * kTile, kbase, vbase, page_stride);
-          if (t + 3 < ntiles) chunk_pages<D, P>(pg, tid, (t + 3) * kTile, last, btrow);
-        }
-        if (t + 1 < ntiles) chunk_qk<D>(sm, buf1, n, g, qb, nxt);
-        chunk_softmax<D>(cur, t * kTile, g, t * kTile + kTile > wave_lim, lim, a.score_scale, m_run,
-                         lacc, o, pk);
-        chunk_pv<D>(sm, buf, n, g, pk, lacc, o);
-        if (t + 2 < ntiles) chunk_store<D>(sm, buf2, regs, tid, (t + 2) * kTile, L);
-        __syncthreads();
-        buf = buf1;
+        if (t * kTile + kTile > wave_lim)
+          body(std::true_type{}, t, cur, nxt);
+        else
+          body(std::false_type{}, t, cur, nxt);
       }
     }
+  }
+  // bring the state to the true row maxima
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const float fac = (m_max[nb] == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_max[nb]);
+    lacc[nb] *= fac;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) o[nb][blk] *= fac;
   }
 
   // ---- normalise and write fp16 rows (lane holds dims 16*blk + 4g + i of row n)
