@@ -419,7 +419,7 @@ def main():
             k_src = torch.from_numpy(bt.k).cuda()
             v_src = torch.from_numpy(bt.v).cuda()
             calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
-            S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()))
+            S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens)
             nsets, steps = 2, max(10, args.steps // 3)
         elif p == "mixed":
             from synth.workloads import make_mixed_calibration

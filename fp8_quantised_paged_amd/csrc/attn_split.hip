@@ -46,6 +46,82 @@ __device__ __forceinline__ float wave_sum_groups(float x) {
   return x;
 }
 
+// One (sequence, kv-head, split) work item.
+struct SplitItem {
+  int b, kvh, s;
+  int L;       // the sequence's context length
+  int n_used;  // splits the sequence uses (the rest of its S slots are empty)
+  int chunk;   // keys per split
+  bool valid;
+};
+
+// The work plan, computed identically by every wavefront of every workgroup
+// from the context lengths alone. All sequences share one split size, set by
+// the longest context: C = ceil(L_max / (64 S)) * 64 keys, so the longest
+// sequence uses all S splits and a shorter one only ceil(L / C) of them (at
+// least one). The non-empty items are numbered in order of sequence, kv-head
+// and split, and workgroup `item` takes the item of that number; numbers past
+// the last item get none. So the workgroups that have work come first in
+// dispatch order and spread evenly over the compute units, and when every
+// sequence has the same length the plan is the plain (split, kv-head,
+// sequence) grid.
+// Wave-wide integer max and inclusive prefix sum with DPP row shifts and the
+// gfx9 row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ int wave_incl_sum_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+__device__ __forceinline__ SplitItem plan_item(const int32_t* __restrict__ seq_lens, int batch, int n_kv_heads,
+                                               int S, int item, int lane) {
+  const int L0 = lane < batch ? seq_lens[lane] : 0;
+  int lmax = L0;
+  for (int i = lane + 64; i < batch; i += 64) lmax = max(lmax, seq_lens[i]);
+  lmax = wave_max_i32(lmax);
+  SplitItem it;
+  it.chunk = max(kTile, ((lmax + kTile * S - 1) / (kTile * S)) * kTile);
+  it.valid = false;
+  it.b = it.kvh = it.s = it.L = it.n_used = 0;
+  int base = 0;  // items of the sequences before b0
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int bb = b0 + lane;
+    const int Lb = b0 == 0 ? L0 : (bb < batch ? seq_lens[bb] : 0);
+    const int used = bb < batch ? max(1, (Lb + it.chunk - 1) / it.chunk) : 0;
+    const int c = used * n_kv_heads;
+    const int incl = wave_incl_sum_i32(c);  // items of sequences b0 .. bb
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (item < base + total) {
+      const uint64_t hit = __ballot(base + incl > item);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      const int r = item - base - __builtin_amdgcn_readlane(incl - c, src);
+      it.n_used = __builtin_amdgcn_readlane(used, src);
+      it.L = __builtin_amdgcn_readlane(Lb, src);
+      it.b = b0 + src;
+      it.kvh = r / it.n_used;
+      it.s = r % it.n_used;
+      it.valid = true;
+      break;
+    }
+    base += total;
+  }
+  return it;
+}
+
 // Per-lane page ids of one 64-key tile: the page of this lane's K rows (one per
 // M-tile when pages are shorter than 16 keys) and of its 16 V keys (one per
 // piece of P keys when P < 16). Indices are clamped to the sequence's last
@@ -334,11 +410,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-
-  const int L = a.seq_lens[b];
+  const int S = a.num_splits;
+  const SplitItem itm = plan_item(a.seq_lens, a.batch, a.n_kv_heads, S,
+                                  blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), lane);
+  if (!itm.valid) return;  // past the last item (uniform over the workgroup)
+  const int s = itm.s;
+  const int kvh = itm.kvh;
+  const int b = itm.b;
+  const int L = itm.L;
   int q0, T;
   if (a.cu_q_lens != nullptr) {
     q0 = a.cu_q_lens[b];
@@ -350,11 +429,25 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   T = min(T, a.max_q_len);
   const int G = a.group;
   const int nrows = T * G;
-  const int S = a.num_splits;
-  const int chunk = ((L + kTile * S - 1) / (kTile * S)) * kTile;
-  const int start = s * chunk;
-  const int end = min(start + chunk, L);
+  const int start = s * itm.chunk;
+  const int end = min(start + itm.chunk, L);
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
+  // the sequence's last item also marks its unused split slots as empty
+  // (m = -inf, l = 0: weight zero in the reduce, which never multiplies their o)
+  const int s_fill_end = (s == itm.n_used - 1) ? S : s + 1;
+
+  // An item with no keys (a sequence of length 0) writes only m and l.
+  if (ntiles == 0 && a.out == nullptr) {
+    for (int rr = threadIdx.x; rr < nrows; rr += 64 * W) {
+      const int i = rr / G;
+      const int64_t unit = ((int64_t)(q0 + i) * a.n_q_heads + kvh * G + rr % G) * S;
+      for (int s2 = s; s2 < s_fill_end; ++s2) {
+        a.ws_m[unit + s2] = -INFINITY;
+        a.ws_l[unit + s2] = 0.0f;
+      }
+    }
+    return;
+  }
 
   // ---- append (decode only): the wavefront that will load the tile holding
   // key L - 1 first quantises the sequence's new token into that slot, exactly
@@ -578,6 +671,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
       if (dg == 0) {
         a.ws_m[unit] = (M == -INFINITY) ? -INFINITY : M * kLn2;
         a.ws_l[unit] = lsum;
+        for (int s2 = s + 1; s2 < s_fill_end; ++s2) {
+          a.ws_m[unit - s + s2] = -INFINITY;
+          a.ws_l[unit - s + s2] = 0.0f;
+        }
       }
     }
   }

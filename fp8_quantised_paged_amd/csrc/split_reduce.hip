@@ -62,20 +62,27 @@ __global__ __launch_bounds__(64 * kWaves) void split_reduce_kernel(
     den += w * ls[k];
   }
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  // splits past the last one with a finite m have weight zero: their o is
+  // neither loaded nor used (their slots need not have been written)
+  int n_live = 0;
+#pragma unroll
+  for (int k = 0; k < SPL; ++k)
+    if (ms[k] != -INFINITY) n_live = lane + 64 * k + 1;
+  for (int off = 32; off > 0; off >>= 1) n_live = max(n_live, __shfl_xor(n_live, off));
   __syncthreads();
 
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
-  while (s0 < num_splits) {
+  while (s0 < n_live) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float w = (s0 + u < num_splits) ? wsh[s0 + u] : 0.0f;
+      const float w = (s0 + u < n_live) ? wsh[s0 + u] : 0.0f;
 #pragma unroll
       for (int j = 0; j < PER; ++j) acc[j] += (w != 0.0f) ? w * v[u][j] : 0.0f;
     }
     s0 += kWaves * kBatch;
-    if (s0 >= num_splits) break;
+    if (s0 >= n_live) break;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int s = min(s0 + u, num_splits - 1);

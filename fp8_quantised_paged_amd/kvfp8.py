@@ -126,16 +126,35 @@ def kvfp8_attn_workspace_bytes(n_rows: int, n_q_heads: int, head_dim: int, num_s
 
 
 def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Optional[int] = None,
-                   cus: int = 256) -> int:
+                   cus: int = 256, seq_lens=None) -> int:
     """Split count for the split kernel (host-side heuristic).
 
-    Aims for about two workgroups per compute unit with equal work: the keys
-    of all sequences (total_keys, the sum of the context lengths, when the
-    caller knows it; batch * max_seq_len otherwise) are divided into 2 * cus
-    shares, and the longest sequence is split into shares of that size. Splits
-    hold at least 512 keys; at most 256 splits."""
+    Aims for at most two workgroups per compute unit (the split kernel's
+    occupancy) with equal work. All sequences of a call share one split size,
+    set by the longest context and the split count, so a shorter sequence
+    fills fewer splits. With the context lengths known on the host
+    (seq_lens), this returns the largest split count whose non-empty splits,
+    over all sequences and kv-heads, fit in 2 * cus workgroups. Otherwise the
+    keys (total_keys, or batch * max_seq_len) are divided into 2 * cus shares
+    and the longest sequence is split into shares of that size. Splits hold
+    at least 512 keys (unless there is only one); at most 256 splits."""
     slots = 2 * cus
-    total = (total_keys if total_keys is not None else batch * max_seq_len) * max(1, n_kv_heads)
+    heads = max(1, n_kv_heads)
+    if seq_lens is not None:
+        lens = [int(x) for x in seq_lens]
+        lmax = max(lens) if lens else 0
+        if lmax <= 0:
+            return 1
+        best, best_used = 1, 0
+        for s in range(1, 257):
+            chunk = -(-lmax // (64 * s)) * 64
+            if chunk < 512 and s > 1:
+                break
+            used = sum(-(-L // chunk) for L in lens if L > 0) * heads
+            if best_used < used <= slots:  # ties keep the smaller count (fewer empty splits)
+                best, best_used = s, used
+        return best
+    total = (total_keys if total_keys is not None else batch * max_seq_len) * heads
     share = max(512, -(-total // slots))
     s = -(-max(1, max_seq_len) // share)
     return int(max(1, min(s, 256)))

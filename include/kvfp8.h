@@ -74,7 +74,8 @@ const char* kvfp8_last_error(void);
  *   ws_o [n_rows][n_q_heads][num_splits][head_dim]  unnormalised, v_scale applied
  *   ws_m [n_rows][n_q_heads][num_splits]            running max, natural-log units
  *   ws_l [n_rows][n_q_heads][num_splits]            sum of exp(score - m)
- * An empty split holds m = -inf, l = 0, o = 0. The workspace is FP32 by
+ * An empty split holds m = -inf and l = 0; its o slot is not written (the
+ * reduce gives it weight zero and never multiplies it). The workspace is FP32 by
  * contract ([P1] Status and history and [P3] Problem and resulting behavior:
  * a half-precision split temporary broke the E4M3 route). Calls sharing one
  * workspace must not overlap. Returns 0 for non-positive arguments. */
@@ -115,8 +116,12 @@ int32_t kv_quant_write(const uint16_t* k_f16, const uint16_t* v_f16, const int64
  * decode and split routes over the E4M3 cache). q_f16: [batch][n_q_heads]
  * [head_dim] fp16; block_table: [batch][max_pages_per_seq] int32; seq_lens:
  * [batch] int32 (>= 1). out_f16: [batch][n_q_heads][head_dim] fp16.
- * num_splits >= 1 splits every sequence's keys into num_splits ranges of
- * ceil(L / (64 * num_splits)) * 64 keys (the last may be shorter or empty).
+ * num_splits >= 1 splits the keys of every sequence into ranges of one size
+ * for the whole call, C = ceil(L_max / (64 * num_splits)) * 64 keys with L_max
+ * the longest context of the batch: split s covers keys [s*C, min((s+1)*C, L)),
+ * so the longest sequence uses all num_splits splits and a shorter one
+ * ceil(L / C) of them (the others are empty). In a ragged batch every
+ * non-empty split then carries the same work.
  * num_splits == 1 writes out_f16 directly (workspace may be NULL). With
  * num_splits > 1 the FP32 partials go to `workspace` (see
  * kvfp8_attn_workspace_bytes) and, when out_f16 is not NULL, split_reduce_fp32
@@ -182,7 +187,9 @@ int32_t paged_attn_e4m3_verify(const uint16_t* q_f16, const int32_t* cu_q_lens, 
  * workspace, whose three parts may also come from elsewhere, e.g. partials
  * gathered from context shards). out_f16: [n_rows][n_q_heads][head_dim] fp16;
  * lse_out: [n_rows][n_q_heads] fp32 or NULL. A row whose splits are all empty
- * gets out = 0 and lse = -inf. head_dim 64 or 128; 1 <= num_splits <= 256. */
+ * gets out = 0 and lse = -inf. Only splits up to the last one with a finite m
+ * are read in full: o of the splits after it need not have been written.
+ * head_dim 64 or 128; 1 <= num_splits <= 256. */
 int32_t split_reduce_fp32(const float* ws_o, const float* ws_m, const float* ws_l, int32_t n_rows,
                           int32_t n_q_heads, int32_t head_dim, int32_t num_splits, uint16_t* out_f16,
                           float* lse_out, hipStream_t stream);

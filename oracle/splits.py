@@ -19,9 +19,14 @@ l_s = 0, o_s = 0. The reduction is
 
 which equals the unsplit softmax for any partition of the keys.
 
-Split boundaries (reading): split s of a sequence with L keys and S splits
-covers [s * C, min((s + 1) * C, L)) with C = ceil(L / (S * granule)) * granule,
-so every split but the last starts on a multiple of the granule.
+Split boundaries (reading; the pages fix only that the split partials are
+FP32, not where the splits fall): all sequences of one call share one split
+size, set by the longest context of the batch, L_max. Split s of a sequence
+with L keys covers [s * C, min((s + 1) * C, L)) with
+C = ceil(L_max / (S * granule)) * granule, so every split but the last starts
+on a multiple of the granule, the longest sequence uses all S splits, and a
+shorter one uses ceil(L / C) of them (the rest are empty). Equal work per
+non-empty split is what lets a ragged batch spread over the whole device.
 """
 
 import numpy as np
@@ -29,11 +34,16 @@ import numpy as np
 from .attention import gather_sequence_kv
 
 
-def split_bounds(seq_len: int, num_splits: int, granule: int = 64):
-    """[(start, end)] key ranges of each split (end <= start means empty)."""
+def split_bounds(seq_len: int, num_splits: int, granule: int = 64, max_len=None):
+    """[(start, end)] key ranges of each split (end <= start means empty).
+
+    max_len is the longest context of the batch (seq_len itself when None)."""
     L = int(seq_len)
+    Lm = L if max_len is None else int(max_len)
+    if Lm < L:
+        raise ValueError("max_len must be at least seq_len")
     S = int(num_splits)
-    chunk = -(-L // (S * granule)) * granule if L > 0 else granule
+    chunk = -(-Lm // (S * granule)) * granule if Lm > 0 else granule
     return [(s * chunk, min((s + 1) * chunk, L)) for s in range(S)]
 
 
@@ -52,6 +62,7 @@ def split_partials(q_f16, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
     ws_o = np.full((total_q, n_q_heads, S, head_dim), np.nan)
     ws_m = np.full((total_q, n_q_heads, S), np.nan)
     ws_l = np.full((total_q, n_q_heads, S), np.nan)
+    max_len = int(np.max(seq_lens)) if len(seq_lens) else 0
     for b in (range(len(seq_lens)) if rows is None else rows):
         L = int(seq_lens[b])
         q0, q1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
@@ -63,7 +74,7 @@ def split_partials(q_f16, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
         vd = vd * vs
         for i in range(T):
             pos = L - T + i
-            for s, (lo, hi) in enumerate(split_bounds(L, S, granule)):
+            for s, (lo, hi) in enumerate(split_bounds(L, S, granule, max_len)):
                 hi = min(hi, pos + 1)
                 r = q0 + i
                 if hi <= lo:

@@ -171,6 +171,9 @@ DECODE_CASES = {
     "d128_p64_g4": lambda: make_batch([700, 64, 129], [1] * 3, 16, 4, 128, 64, seed=53),
     "d128_p32_g16": lambda: make_batch([300, 41], [1] * 2, 32, 2, 128, 32, seed=54),
     "d64_p4_g32": lambda: make_batch([90, 17], [1] * 2, 32, 1, 64, 4, seed=55),
+    # more than 64 sequences: the split plan's prefix count runs over several blocks of 64
+    "d128_b150_ragged": lambda: make_batch([1 + (37 * i) % 300 for i in range(150)], [1] * 150, 32, 4, 128, 16,
+                                           seed=56),
 }
 
 
@@ -270,8 +273,12 @@ def test_partials_match_oracle_partials(K):
     fin = np.isfinite(rm)
     np.testing.assert_allclose(m[fin], rm[fin], rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(l, rl, rtol=2e-3, atol=1e-5)
+    # an empty split writes m = -inf and l = 0 only: its o slot keeps the poison
     scale = np.maximum(rl[..., None], 1.0)
-    assert (np.abs(o - ro) <= 2e-3 * scale + 1e-2 * np.abs(ro)).all()
+    assert (np.abs(o - ro) <= 2e-3 * scale + 1e-2 * np.abs(ro))[fin].all()
+    assert np.isnan(o[~fin]).all()
+    # the ragged lengths leave empty splits in the shorter sequences
+    assert (~fin).any() and fin[:, :, 1].any()
 
 
 def test_split_reduce_of_oracle_partials(K):
@@ -286,6 +293,33 @@ def test_split_reduce_of_oracle_partials(K):
     out, lse = K.split_reduce_fp32(dev(o32), dev(m32), dev(l32), with_lse=True)
     assert_close_attn(out.cpu().numpy(), ref, "reduce")
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("S", [3, 20, 70])
+def test_split_reduce_ignores_o_of_empty_splits(K, S):
+    """Empty splits (m = -inf, l = 0) may hold anything in o: before, between
+    and after live splits, NaN there must not reach the output."""
+    rng = np.random.default_rng(73 + S)
+    R, H, D = 3, 4, 128
+    m = rng.uniform(-3, 3, (R, H, S)).astype(np.float32)
+    l = rng.uniform(0.5, 4, (R, H, S)).astype(np.float32)
+    o = rng.standard_normal((R, H, S, D)).astype(np.float32)
+    dead = rng.random((R, H, S)) < 0.5
+    dead[0, 0, :] = True           # a row with no live split
+    dead[1, 1, :] = False
+    dead[1, 1, S - 1] = True       # trailing empty split
+    dead[2, 2, :] = True
+    dead[2, 2, S // 2] = False     # one live split in the middle
+    m[dead], l[dead], o[dead] = -np.inf, 0.0, 0.0
+    ref, ref_lse = split_reduce(o.astype(np.float64), m, l)  # an empty split's o is 0 by definition
+    o[dead] = np.nan
+    out, lse = K.split_reduce_fp32(dev(o), dev(m), dev(l), with_lse=True)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all()
+    assert (out[0, 0] == 0).all() and np.isneginf(lse[0, 0])
+    assert_close_attn(out, ref, f"reduce S={S}")
+    fin = np.isfinite(ref_lse)
+    np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-5, atol=1e-5)
 
 
 def test_split_reduce_all_empty_rows(K):

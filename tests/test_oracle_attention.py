@@ -163,13 +163,31 @@ def test_poisoned_slots_never_reach_outputs():
 def test_split_bounds_partition():
     for L in (1, 63, 64, 65, 100, 257, 4096, 32768, 262144):
         for S in (1, 2, 3, 7, 64):
-            b = split_bounds(L, S)
-            covered = []
-            for lo, hi in b:
-                if hi > lo:
-                    assert lo % 64 == 0
-                    covered.extend(range(lo, hi))
-            assert covered == list(range(L))
+            for Lm in (L, L + 1, 3 * L, 262144):
+                b = split_bounds(L, S, max_len=Lm)
+                covered = []
+                for lo, hi in b:
+                    if hi > lo:
+                        assert lo % 64 == 0
+                        covered.extend(range(lo, hi))
+                assert covered == list(range(L))
+
+
+def test_split_bounds_share_one_size():
+    """Every non-empty split but a sequence's last has the same size, set by
+    the longest context; the longest sequence uses all S splits."""
+    lens = [1024, 4096, 8192, 32768, 100, 1]
+    S = 19
+    C = -(-32768 // (S * 64)) * 64
+    assert C == 1728
+    for L in lens:
+        b = split_bounds(L, S, max_len=max(lens))
+        sizes = [hi - lo for lo, hi in b if hi > lo]
+        assert len(sizes) == -(-L // C)
+        assert all(x == C for x in sizes[:-1]) and 0 < sizes[-1] <= C
+    assert len([1 for lo, hi in split_bounds(32768, S, max_len=32768) if hi > lo]) == S
+    with pytest.raises(ValueError):
+        split_bounds(100, 2, max_len=99)
 
 
 @pytest.mark.parametrize("S", [1, 2, 3, 7, 64])
