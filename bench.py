@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # FETCH_SIZE / WRITE_SIZE runs (`bench.py --counter-pass`), scaled by the same
 # counters' reading of a 1 GiB device copy. Valid only for the kernel source
 # they were taken on (sha256 prefix); otherwise the traffic is reported as null.
-MEASURED_TRAFFIC = {"source_sha256_prefix": "878e7af452e9ff96", "read_bytes": 137213374,
+MEASURED_TRAFFIC = {"source_sha256_prefix": "752df7cc0bd222a5", "read_bytes": 137243198,
                     "write_bytes": 2228224}
 
 
