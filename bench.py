@@ -371,7 +371,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed")
+    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed,4k_p4")
     ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=60)
@@ -414,6 +414,16 @@ def main():
             calib = cal.view(2, -1)
             S = K.default_splits(bt.batch, bt.n_kv_heads, 32768)
             nsets, steps = 2, max(10, args.steps // 3)
+        elif p == "4k_p4":
+            # derived: the 4k decode shape with the pages' grouped page-size-4 layout
+            bt = make_config(2, values=False, page_size_override=4)
+            total = int(bt.cu_seq_lens[-1])
+            k_src = normal_kv(total, 4, 128, bt.seed * 10 + 1)
+            v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2)
+            cal = normal_kv(2 * 2048, 4, 128, bt.seed * 10 + 3)
+            calib = cal.view(2, -1)
+            S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)
+            nsets, steps = 6, args.steps
         elif p == "mtp3":
             bt = make_config(3)
             k_src = torch.from_numpy(bt.k).cuda()

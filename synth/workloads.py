@@ -199,7 +199,7 @@ def mtp3_context_lengths(seed: int, batch: int = 16) -> np.ndarray:
 
 
 def make_config(idx: int, layer: int = 0, seq_len_override: Optional[int] = None,
-                values: bool = True) -> PagedBatch:
+                values: bool = True, page_size_override: Optional[int] = None) -> PagedBatch:
     """The five named workloads. For the mixed workload (5) one layer's batch is
     returned: 8 decode sequences at 8,192 followed by one sequence holding a
     2,048-token chunk over a 30,000-token prior context."""
@@ -208,7 +208,7 @@ def make_config(idx: int, layer: int = 0, seq_len_override: Optional[int] = None
         return make_batch([100, 257], [1, 1], 8, 2, 64, 4, seed, name=CONFIG_NAMES[1], values=values)
     if idx == 2:
         L = seq_len_override or 4096
-        return make_batch([L] * 32, [1] * 32, 32, 4, 128, 16, seed, name=CONFIG_NAMES[2],
+        return make_batch([L] * 32, [1] * 32, 32, 4, 128, page_size_override or 16, seed, name=CONFIG_NAMES[2],
                           calib_tokens=2048, values=values)
     if idx == 3:
         lens = mtp3_context_lengths(seed)
