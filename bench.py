@@ -39,17 +39,23 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # FETCH_SIZE / WRITE_SIZE runs (`bench.py --counter-pass`), scaled by the same
 # counters' reading of a 1 GiB device copy. Valid only for the kernel source
 # they were taken on (sha256 prefix); otherwise the traffic is reported as null.
-MEASURED_TRAFFIC = {"source_sha256_prefix": "752df7cc0bd222a5", "read_bytes": 137243198,
+MEASURED_TRAFFIC = {"source_sha256_prefix": "a1237481a2ff49e4", "read_bytes": 137243198,
                     "write_bytes": 2228224}
+
+
+TRAFFIC_SOURCES = ("attn_split.hip", "split_plan.h")  # the sources the counted kernel is built from
 
 
 def measured_traffic():
     import hashlib
-    src = os.path.join(ROOT, "fp8_quantised_paged_amd", "csrc", "attn_split.hip")
+    csrc = os.path.join(ROOT, "fp8_quantised_paged_amd", "csrc")
+    h = hashlib.sha256()
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        for name in TRAFFIC_SOURCES:
+            h.update(open(os.path.join(csrc, name), "rb").read())
     except OSError:
         return None
+    sha = h.hexdigest()[:16]
     if sha != MEASURED_TRAFFIC["source_sha256_prefix"]:
         return None
     return MEASURED_TRAFFIC["read_bytes"] + MEASURED_TRAFFIC["write_bytes"]
@@ -60,13 +66,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(seq_lens, n_q_heads, n_kv_heads, head_dim, max_pages, q_rows=None):
+def algorithmic_bytes(seq_lens, n_q_heads, n_kv_heads, head_dim, max_pages, q_rows=None, kv_elem_bytes=1):
     """Bytes one decode (or verify) step must move at minimum: every cached K
-    and V byte, Q in, O out (fp16, q_rows query rows, one per sequence unless
-    given), the block table and the sequence lengths."""
+    and V byte (kv_elem_bytes per element: 1 for E4M3, 2 for the fp16 arm),
+    Q in, O out (fp16, q_rows query rows, one per sequence unless given), the
+    block table and the sequence lengths."""
     B = len(seq_lens)
     rows = B if q_rows is None else int(q_rows)
-    kv = int(np.sum(seq_lens, dtype=np.int64)) * n_kv_heads * head_dim * 2
+    kv = int(np.sum(seq_lens, dtype=np.int64)) * n_kv_heads * head_dim * 2 * kv_elem_bytes
     qo = 2 * rows * n_q_heads * head_dim * 2
     meta = B * max_pages * 4 + B * 4
     return kv, kv + qo + meta
@@ -75,11 +82,14 @@ def algorithmic_bytes(seq_lens, n_q_heads, n_kv_heads, head_dim, max_pages, q_ro
 class Point:
     """One decode workload resident on the GPU with `nsets` cache copies."""
 
-    def __init__(self, K, torch, name, layout, k_src, v_src, calib, num_splits, nsets, scales=None):
+    def __init__(self, K, torch, name, layout, k_src, v_src, calib, num_splits, nsets, scales=None, f16=False):
         self.K, self.torch, self.name, self.bt = K, torch, name, layout
         bt = layout
         dev = "cuda"
         self.S = num_splits
+        self.f16 = f16  # the fp16-cache arm of the format comparison
+        if f16:
+            scales = (1.0, 1.0)
         self.B, self.Hq, self.Hkv, self.D, self.P = bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.page_size
         if scales is None:
             amax, scale, _ = K.kv_calibrate_amax(calib)
@@ -100,22 +110,38 @@ class Point:
         self.slots_new = slots[new_rows].contiguous()
         self.sets = []
         for _ in range(nsets):
-            kc = torch.full((bt.num_pages, self.Hkv, self.P, self.D), 0x7F, dtype=torch.uint8, device=dev)
-            vc = torch.full((bt.num_pages, self.Hkv, self.D, self.P), 0x7F, dtype=torch.uint8, device=dev)
-            K.kv_quant_write(k_src, v_src, slots, self.ks, self.vs, kc, vc)
+            if f16:
+                # cache fill (setup): fp16 values scattered to their slots, NaN elsewhere
+                kc = torch.full((bt.num_pages, self.Hkv, self.P, self.D), float("nan"), dtype=torch.float16,
+                                device=dev)
+                vc = torch.full((bt.num_pages, self.Hkv, self.D, self.P), float("nan"), dtype=torch.float16,
+                                device=dev)
+                pg, off = slots // self.P, slots % self.P
+                kc[pg, :, off, :] = k_src
+                vc[pg, :, :, off] = v_src
+            else:
+                kc = torch.full((bt.num_pages, self.Hkv, self.P, self.D), 0x7F, dtype=torch.uint8, device=dev)
+                vc = torch.full((bt.num_pages, self.Hkv, self.D, self.P), 0x7F, dtype=torch.uint8, device=dev)
+                K.kv_quant_write(k_src, v_src, slots, self.ks, self.vs, kc, vc)
             self.sets.append((kc, vc))
         self.ws = K.workspace(self.rows, self.Hq, self.D, self.S)
         self.ws_o, self.ws_m, self.ws_l = K.workspace_views(self.ws, self.rows, self.Hq, self.D, self.S)
         self.out = torch.empty_like(self.q)
         self.kv_bytes, self.alg_bytes = algorithmic_bytes(bt.seq_lens, self.Hq, self.Hkv, self.D,
-                                                          bt.max_pages, q_rows=self.rows)
+                                                          bt.max_pages, q_rows=self.rows,
+                                                          kv_elem_bytes=2 if f16 else 1)
         torch.cuda.synchronize()
 
     def _call(self, i, out):
         kc, vc = self.sets[i % len(self.sets)]
         kw = dict(num_splits=self.S, workspace=self.ws)
         kw.update(out=out) if out is not None else kw.update(partials_only=True)
-        if self.verify:
+        if self.f16 and self.verify:
+            self.K.paged_attn_f16_verify(self.q, self.cu_q, self.max_q, kc, vc, self.block_table, self.seq_lens,
+                                         self.sm, **kw)
+        elif self.f16:
+            self.K.paged_attn_f16_decode(self.q, kc, vc, self.block_table, self.seq_lens, self.sm, **kw)
+        elif self.verify:
             self.K.paged_attn_e4m3_verify(self.q, self.cu_q, self.max_q, kc, vc, self.block_table,
                                           self.seq_lens, self.ks, self.vs, self.sm, **kw)
         else:
@@ -127,9 +153,11 @@ class Point:
         self._call(i, None)
 
     def step(self, i):
-        """Write kernel, then attention (and the reduce when split)."""
+        """Write kernel, then attention (and the reduce when split). The fp16
+        arm has no write kernel: its step is attention and reduce."""
         kc, vc = self.sets[i % len(self.sets)]
-        self.K.kv_quant_write(self.k_new, self.v_new, self.slots_new, self.ks, self.vs, kc, vc)
+        if not self.f16:
+            self.K.kv_quant_write(self.k_new, self.v_new, self.slots_new, self.ks, self.vs, kc, vc)
         self._call(i, self.out)
 
     def step_fused(self, i):
@@ -371,7 +399,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed,4k_p4")
+    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed,4k_p4,4k_f16,mtp3_f16")
     ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=60)
@@ -424,6 +452,16 @@ def main():
             calib = cal.view(2, -1)
             S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)
             nsets, steps = 6, args.steps
+        elif p in ("4k_f16", "mtp3_f16"):
+            # the fp16-cache arm of the format comparison, on the 4k decode and MTP3 shapes
+            bt = make_config(2 if p == "4k_f16" else 3, values=False)
+            total = int(bt.cu_seq_lens[-1])
+            k_src = normal_kv(total, 4, 128, bt.seed * 10 + 1)
+            v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2)
+            calib = None
+            S = (K.default_splits(bt.batch, bt.n_kv_heads, 4096) if p == "4k_f16" else
+                 K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens))
+            nsets, steps = (6, args.steps) if p == "4k_f16" else (2, max(10, args.steps // 3))
         elif p == "mtp3":
             bt = make_config(3)
             k_src = torch.from_numpy(bt.k).cuda()
@@ -465,12 +503,12 @@ def main():
             nsets, steps = 2, max(10, args.steps // 3)
         else:
             raise SystemExit(f"unknown point {p}")
-        pt = Point(K, torch, p, bt, k_src, v_src, calib, S, nsets)
+        pt = Point(K, torch, p, bt, k_src, v_src, calib, S, nsets, f16=p.endswith("_f16"))
         del k_src, v_src
         torch.cuda.empty_cache()
         log(f"{p}: batch {pt.B} splits {S} kv bytes {pt.kv_bytes}; timing {steps} steps")
         sec_sep, wall_sep, same_sep = pt.time_steps(steps, args.warmup)
-        if pt.verify:
+        if pt.verify or pt.f16:
             sec, wall, same = sec_sep, wall_sep, same_sep
         else:
             sec, wall, same = pt.time_steps(steps, args.warmup, fused=True)
@@ -485,7 +523,9 @@ def main():
             "kv_bytes_per_step": pt.kv_bytes, "algorithmic_bytes_per_step": pt.alg_bytes,
             "kv_gbs": pt.kv_bytes / sec / 1e9, "tokens_per_s_per_layer": pt.rows / sec,
             "ms_per_step_separate_write": sec_sep * 1e3,
-            "step": "separate write + attention" if pt.verify else "attention with the new tokens appended",
+            "step": ("attention + reduce over fp16 pages (no write)" if pt.f16 else
+                     "separate write + attention" if pt.verify else "attention with the new tokens appended"),
+            "kv_cache": "fp16" if pt.f16 else "e4m3",
             "attn_kernel_us": kern * 1e6, "attn_kernel_gbs": pt.alg_bytes / kern / 1e9,
             "graph_replay_matches_eager": same, "cache_sets": nsets,
         }

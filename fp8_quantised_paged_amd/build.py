@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvfp8.so")
-SOURCES = ["api.cpp", "scale_overlay.cpp", "calibrate.hip", "quant_write.hip", "attn_split.hip",
+SOURCES = ["api.cpp", "scale_overlay.cpp", "calibrate.hip", "quant_write.hip", "attn_split.hip", "attn_split_f16.hip",
            "attn_chunk.hip", "split_reduce.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -149,7 +149,7 @@ struct AppendArgs {
 };
 
 int32_t run_attention(const AttnCommon& c, const int32_t* cu_q, int64_t n_rows, int32_t max_q,
-                      hipStream_t stream, const AppendArgs* app = nullptr) {
+                      hipStream_t stream, const AppendArgs* app = nullptr, bool f16_kv = false) {
   if (c.batch == 0 || n_rows == 0) return ok();
   const int32_t group = c.n_q_heads / c.n_kv_heads;
   const int64_t rows = (int64_t)max_q * group;
@@ -161,7 +161,11 @@ int32_t run_attention(const AttnCommon& c, const int32_t* cu_q, int64_t n_rows, 
     a.v_cache_w = app->v_cache;
   }
   hipError_t e;
-  if (rows <= kSplitRows) {
+  if (f16_kv) {
+    if (rows > kSplitRows)
+      return fail(KVFP8_UNSUPPORTED, "the fp16-cache kernel takes at most %d query rows per kv-head", kSplitRows);
+    e = kvfp8::launch_attn_split_f16(a, (int)rows, stream);
+  } else if (rows <= kSplitRows) {
     e = kvfp8::launch_attn_split(a, (int)rows, stream);
   } else {
     if (c.num_splits != 1)
@@ -318,6 +322,43 @@ KVFP8_API int32_t paged_attn_e4m3_verify(const uint16_t* q_f16, const int32_t* c
   int32_t st = check_common(c, total_q);
   if (st != KVFP8_OK) return st;
   return run_attention(c, cu_q_lens, total_q, max_q_len, stream);
+}
+
+KVFP8_API int32_t paged_attn_f16_decode(const uint16_t* q_f16, const uint16_t* k_cache_f16,
+                                        const uint16_t* v_cache_f16, const int32_t* block_table,
+                                        const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                        int32_t max_pages_per_seq, float sm_scale, int32_t num_splits,
+                                        float* workspace, size_t workspace_bytes, uint16_t* out_f16,
+                                        hipStream_t stream) {
+  AttnCommon c{q_f16, reinterpret_cast<const uint8_t*>(k_cache_f16), reinterpret_cast<const uint8_t*>(v_cache_f16),
+               block_table, seq_lens, batch, n_q_heads, n_kv_heads, head_dim, page_size, max_pages_per_seq,
+               1.0f, 1.0f, sm_scale, num_splits, workspace, workspace_bytes, out_f16};
+  int32_t st = check_common(c, batch);
+  if (st != KVFP8_OK) return st;
+  if (n_q_heads / n_kv_heads > kSplitRows)
+    return fail(KVFP8_UNSUPPORTED, "GQA group of %d heads (at most %d)", n_q_heads / n_kv_heads,
+                kSplitRows);
+  return run_attention(c, nullptr, batch, 1, stream, nullptr, true);
+}
+
+KVFP8_API int32_t paged_attn_f16_verify(const uint16_t* q_f16, const int32_t* cu_q_lens, int32_t total_q,
+                                        int32_t max_q_len, const uint16_t* k_cache_f16,
+                                        const uint16_t* v_cache_f16, const int32_t* block_table,
+                                        const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                        int32_t max_pages_per_seq, float sm_scale, int32_t num_splits,
+                                        float* workspace, size_t workspace_bytes, uint16_t* out_f16,
+                                        hipStream_t stream) {
+  AttnCommon c{q_f16, reinterpret_cast<const uint8_t*>(k_cache_f16), reinterpret_cast<const uint8_t*>(v_cache_f16),
+               block_table, seq_lens, batch, n_q_heads, n_kv_heads, head_dim, page_size, max_pages_per_seq,
+               1.0f, 1.0f, sm_scale, num_splits, workspace, workspace_bytes, out_f16};
+  if (!cu_q_lens) return fail(KVFP8_INVALID_ARG, "null cu_q_lens");
+  if (total_q < 0) return fail(KVFP8_INVALID_ARG, "negative total_q");
+  if (max_q_len < 1 && total_q > 0) return fail(KVFP8_INVALID_ARG, "max_q_len must be >= 1");
+  int32_t st = check_common(c, total_q);
+  if (st != KVFP8_OK) return st;
+  return run_attention(c, cu_q_lens, total_q, max_q_len, stream, nullptr, true);
 }
 
 KVFP8_API int32_t split_reduce_fp32(const float* ws_o, const float* ws_m, const float* ws_l,

@@ -95,6 +95,8 @@ hipError_t launch_quant_write(const uint16_t* k, const uint16_t* v, const int64_
                               uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 // Split-context kernel for up to 32 query rows per (sequence, kv-head).
 hipError_t launch_attn_split(const AttnArgs& a, int rows_per_kvh, hipStream_t stream);
+// FP16-KV twin of the split-context kernel (k_cache / v_cache hold fp16).
+hipError_t launch_attn_split_f16(const AttnArgs& a, int rows_per_kvh, hipStream_t stream);
 // Query-tiled causal chunk kernel (long q_len).
 hipError_t launch_attn_chunk(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_split_reduce(const float* ws_o, const float* ws_m, const float* ws_l,

@@ -26,6 +26,8 @@ EXPORTED = (
     "paged_attn_e4m3_decode",
     "paged_attn_e4m3_decode_append",
     "paged_attn_e4m3_verify",
+    "paged_attn_f16_decode",
+    "paged_attn_f16_verify",
     "split_reduce_fp32",
     "kvfp8_attn_workspace_bytes",
     "kvfp8_status_str",
@@ -61,6 +63,9 @@ def _load() -> ctypes.CDLL:
                                                 F32, F32, I32, P, SZ, P, P]),
         "paged_attn_e4m3_verify": (I32, [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                          F32, F32, F32, I32, P, SZ, P, P]),
+        "paged_attn_f16_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32, P, SZ, P, P]),
+        "paged_attn_f16_verify": (I32, [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32,
+                                        P, SZ, P, P]),
         "split_reduce_fp32": (I32, [P, P, P, I32, I32, I32, I32, P, P, P]),
         "kvfp8_e4m3_encode_f32": (I32, [P, P, I64, P]),
         "kvfp8_e4m3_decode_f32": (I32, [P, P, I64, P]),
@@ -323,6 +328,76 @@ def paged_attn_e4m3_verify(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: 
                                        seq_lens.data_ptr(), B, hq, hkv, d, psz, block_table.shape[1],
                                        float(k_scale), float(v_scale), float(sm_scale), int(num_splits),
                                        ws_ptr, ws_bytes, _ptr(out), _stream()), "paged_attn_e4m3_verify")
+    return out
+
+
+def _f16_cache_dims(k_cache, v_cache, q_heads_dim):
+    _need(k_cache, "k_cache", torch.float16, 4)
+    _need(v_cache, "v_cache", torch.float16, 4)
+    pages, hkv, psz, d = k_cache.shape
+    if tuple(v_cache.shape) != (pages, hkv, d, psz):
+        raise ValueError("v_cache must be [pages, Hkv, D, P]")
+    if q_heads_dim != d:
+        raise ValueError("head_dim of q and caches disagree")
+    return hkv, psz, d
+
+
+def paged_attn_f16_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+                          num_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, partials_only: bool = False
+                          ) -> Optional[torch.Tensor]:
+    """Decode over fp16 K/V pages (k_cache [pages, Hkv, P, D], v_cache [pages, Hkv, D, P]); otherwise
+    as paged_attn_e4m3_decode."""
+    _need(q, "q", torch.float16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, hq, d = q.shape
+    hkv, psz, _ = _f16_cache_dims(k_cache, v_cache, d)
+    if partials_only:
+        out = None
+    elif out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16, 3)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.paged_attn_f16_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      block_table.data_ptr(), seq_lens.data_ptr(), B, hq, hkv, d, psz,
+                                      block_table.shape[1], float(sm_scale), int(num_splits), ws_ptr, ws_bytes,
+                                      _ptr(out), _stream()), "paged_attn_f16_decode")
+    return out
+
+
+def paged_attn_f16_verify(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, sm_scale: float, num_splits: int = 1,
+                          workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          partials_only: bool = False) -> Optional[torch.Tensor]:
+    """Multi-query (MTP verify) attention over fp16 K/V pages; otherwise as paged_attn_e4m3_verify
+    (at most 32 query rows per kv-head)."""
+    _need(q, "q", torch.float16, 3)
+    _need(cu_q_lens, "cu_q_lens", torch.int32, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    total_q, hq, d = q.shape
+    B = seq_lens.shape[0]
+    if cu_q_lens.shape[0] != B + 1:
+        raise ValueError("cu_q_lens must have batch + 1 entries")
+    hkv, psz, _ = _f16_cache_dims(k_cache, v_cache, d)
+    if partials_only:
+        out = None
+    elif out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16, 3)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.paged_attn_f16_verify(q.data_ptr(), cu_q_lens.data_ptr(), total_q, int(max_q_len),
+                                      k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                      seq_lens.data_ptr(), B, hq, hkv, d, psz, block_table.shape[1],
+                                      float(sm_scale), int(num_splits), ws_ptr, ws_bytes, _ptr(out), _stream()),
+           "paged_attn_f16_verify")
     return out
 
 

@@ -178,6 +178,27 @@ int32_t paged_attn_e4m3_verify(const uint16_t* q_f16, const int32_t* cu_q_lens, 
                                float v_scale, float sm_scale, int32_t num_splits, float* workspace,
                                size_t workspace_bytes, uint16_t* out_f16, hipStream_t stream);
 
+/* FP16-cache twins of paged_attn_e4m3_decode and paged_attn_e4m3_verify, for
+ * the single-variable comparison of cache formats that the pages make (only
+ * kv_cache_dtype differs between the arms: [P1] Validation on 4xV100 TP4).
+ * k_cache_f16: [num_pages][n_kv_heads][page_size][head_dim] fp16 and
+ * v_cache_f16: [num_pages][n_kv_heads][head_dim][page_size] fp16 (the E4M3
+ * layout with two-byte elements); there are no K/V scales. The work plan, split
+ * boundaries, workspace, reduce, arguments, errors and limits are those of the
+ * E4M3 calls; the verify twin takes at most 32 query rows per kv-head
+ * (max_q_len * group <= 32), larger chunks return KVFP8_UNSUPPORTED. */
+int32_t paged_attn_f16_decode(const uint16_t* q_f16, const uint16_t* k_cache_f16, const uint16_t* v_cache_f16,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t max_pages_per_seq, float sm_scale, int32_t num_splits, float* workspace,
+                              size_t workspace_bytes, uint16_t* out_f16, hipStream_t stream);
+int32_t paged_attn_f16_verify(const uint16_t* q_f16, const int32_t* cu_q_lens, int32_t total_q,
+                              int32_t max_q_len, const uint16_t* k_cache_f16, const uint16_t* v_cache_f16,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t max_pages_per_seq, float sm_scale, int32_t num_splits, float* workspace,
+                              size_t workspace_bytes, uint16_t* out_f16, hipStream_t stream);
+
 /* Reduction of FP32 split partials ([P1] Status and history, [P3] Problem and
  * resulting behavior: the split temporary output is FP32). For each row r and
  * head h, with M = max_s m_s and w_s = exp(m_s - M) (0 for an empty split):

@@ -41,5 +41,5 @@ No function here is "parity unpinned".
 from .e4m3 import e4m3_decode, e4m3_encode, E4M3_MAX  # noqa: F401
 from .calibrate import calibrate_amax, quotient_f32  # noqa: F401
 from .kv_write import quant_write, new_caches, quantise  # noqa: F401
-from .attention import paged_attention, gather_sequence_kv  # noqa: F401
+from .attention import paged_attention, paged_attention_f16, gather_sequence_kv  # noqa: F401
 from .splits import split_partials, split_reduce, split_bounds  # noqa: F401

@@ -40,6 +40,28 @@ def gather_sequence_kv(k_cache, v_cache, block_row, seq_len):
     return e4m3_decode(k_codes), e4m3_decode(v_codes)
 
 
+def gather_sequence_kv_f16(k_cache_f16, v_cache_f16, block_row, seq_len):
+    """K and V of one sequence from fp16 caches (same layout) as float64 [L, Hkv, D]."""
+    page_size = k_cache_f16.shape[2]
+    j = np.arange(int(seq_len))
+    pages = np.asarray(block_row, dtype=np.int64)[j // page_size]
+    offs = j % page_size
+    k = np.asarray(k_cache_f16[pages, :, offs, :], dtype=np.float16).astype(np.float64)
+    v = np.asarray(v_cache_f16[pages, :, :, offs], dtype=np.float16).astype(np.float64)
+    return k, v
+
+
+def paged_attention_f16(q_f16, k_cache_f16, v_cache_f16, block_table, seq_lens, cu_q_lens, sm_scale,
+                        rows=None):
+    """The same attention over a cache that stores fp16 values instead of
+    E4M3 codes (no K/V scales): the other arm of the pages' comparison of cache
+    formats ("Calibrated E4M3 KV cache for Qwen4Exp QSA with MTP", Validation
+    on 4xV100 TP4: only kv_cache_dtype differs between the arms)."""
+    def kv(b, L):
+        return gather_sequence_kv_f16(k_cache_f16, v_cache_f16, block_table[b], L)
+    return _attention(q_f16, k_cache_f16.shape[1], kv, seq_lens, cu_q_lens, sm_scale, rows)
+
+
 def paged_attention(q_f16, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
                     k_scale, v_scale, sm_scale, rows=None):
     """Attention output float64 [total_q, Hq, D] and log-sum-exp [total_q, Hq].
@@ -48,12 +70,20 @@ def paged_attention(q_f16, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
     cu_q_lens[b+1]-1 belong to sequence b). ``rows`` optionally restricts the
     work to a subset of sequences (others are left as NaN).
     """
-    q = np.asarray(q_f16, dtype=np.float16).astype(np.float64)
-    total_q, n_q_heads, head_dim = q.shape
-    n_kv_heads = k_cache.shape[1]
-    group = n_q_heads // n_kv_heads
     ks = float(np.float32(k_scale))
     vs = float(np.float32(v_scale))
+
+    def kv(b, L):
+        kd, vd = gather_sequence_kv(k_cache, v_cache, block_table[b], L)
+        return kd * ks, vd * vs
+    return _attention(q_f16, k_cache.shape[1], kv, seq_lens, cu_q_lens, sm_scale, rows)
+
+
+def _attention(q_f16, n_kv_heads, kv, seq_lens, cu_q_lens, sm_scale, rows):
+    """The definition, given kv(b, L) -> (K, V) float64 [L, Hkv, D] of sequence b."""
+    q = np.asarray(q_f16, dtype=np.float16).astype(np.float64)
+    total_q, n_q_heads, head_dim = q.shape
+    group = n_q_heads // n_kv_heads
     sm = float(np.float32(sm_scale))
     out = np.full((total_q, n_q_heads, head_dim), np.nan)
     lse = np.full((total_q, n_q_heads), np.nan)
@@ -64,9 +94,7 @@ def paged_attention(q_f16, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
         T = q1 - q0
         if T == 0:
             continue
-        kd, vd = gather_sequence_kv(k_cache, v_cache, block_table[b], L)
-        kd = kd * ks
-        vd = vd * vs
+        kd, vd = kv(b, L)
         pos = L - T + np.arange(T)  # position of each query row
         visible = np.arange(L)[None, :] <= pos[:, None]  # [T, L]
         for h in range(n_q_heads):

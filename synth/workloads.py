@@ -234,3 +234,17 @@ def make_mixed_calibration(n_layers: int = 24, tokens: int = 4096, n_kv_heads: i
     for i in range(2 * n_layers):
         out[i] = _normal_f16(np.random.Generator(np.random.PCG64(ss[i])), out.shape[1])
     return out
+
+
+def f16_caches(bt: PagedBatch, poison=np.float16(np.nan)):
+    """fp16 K and V caches of a batch in the paged layout (K [pages][Hkv][P][D],
+    V [pages][Hkv][D][P]) with every token stored at its slot; unused slots hold
+    `poison` (NaN by default). A plain layout scatter: it computes nothing."""
+    P, D, H = bt.page_size, bt.head_dim, bt.n_kv_heads
+    kc = np.full((bt.num_pages, H, P, D), poison, dtype=np.float16)
+    vc = np.full((bt.num_pages, H, D, P), poison, dtype=np.float16)
+    pages = bt.slot_mapping // P
+    offs = bt.slot_mapping % P
+    kc[pages, :, offs, :] = bt.k
+    vc[pages, :, :, offs] = bt.v
+    return kc, vc
