@@ -460,14 +460,16 @@ def main():
             v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2)
             calib = None
             S = (K.default_splits(bt.batch, bt.n_kv_heads, 4096) if p == "4k_f16" else
-                 K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens))
+                 K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
+                                 n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max())))
             nsets, steps = (6, args.steps) if p == "4k_f16" else (2, max(10, args.steps // 3))
         elif p == "mtp3":
             bt = make_config(3)
             k_src = torch.from_numpy(bt.k).cuda()
             v_src = torch.from_numpy(bt.v).cuda()
             calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
-            S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens)
+            S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
+                                 n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
             nsets, steps = 2, max(10, args.steps // 3)
         elif p == "mixed":
             from synth.workloads import make_mixed_calibration
@@ -561,7 +563,7 @@ def main():
                                    if p in ("4k", "32k", "256k")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "attn_split_kernel<128,16,1,4>", "kernel_us": main["attn_kernel_us"]},
+                     "kernel": "attn_split_kernel<128,16,1,8>", "kernel_us": main["attn_kernel_us"]},
         "cpu_baseline": cpu,
         "points": results,
     }

@@ -608,9 +608,20 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
 
 template <int D, int P, int NB>
 hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
-  constexpr int W = 4;
   dim3 grid((unsigned)a.num_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);
-  attn_split_kernel<D, P, NB, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+  // One 16-row block (decode) whose whole grid fits in one round of the
+  // compute units: 8 wavefronts per workgroup, one workgroup per CU, so a CU's
+  // wavefronts are of one age and finish together (two 4-wavefront workgroups
+  // on one CU finish apart under the hardware's oldest-first issue). Larger
+  // grids, and two blocks (verify, LDS-bound), run 4 wavefronts, two
+  // workgroups per CU, which halves the number of rounds.
+  if constexpr (NB == 1) {
+    if ((int64_t)a.num_splits * a.n_kv_heads * a.batch <= device_cus()) {
+      attn_split_kernel<D, P, 1, 8><<<grid, dim3(64 * 8), 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
+  attn_split_kernel<D, P, NB, 4><<<grid, dim3(64 * 4), 0, stream>>>(a);
   return hipGetLastError();
 }
 

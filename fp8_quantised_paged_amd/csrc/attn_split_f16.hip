@@ -387,9 +387,15 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
 
 template <int D, int P, int NB>
 hipError_t launch3_f16(const AttnArgs& a, hipStream_t stream) {
-  constexpr int W = 4;
   dim3 grid((unsigned)a.num_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);
-  attn_split_f16_kernel<D, P, NB, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+  // wavefronts per workgroup chosen as for the E4M3 kernel
+  if constexpr (NB == 1) {
+    if ((int64_t)a.num_splits * a.n_kv_heads * a.batch <= device_cus()) {
+      attn_split_f16_kernel<D, P, 1, 8><<<grid, dim3(64 * 8), 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
+  attn_split_f16_kernel<D, P, NB, 4><<<grid, dim3(64 * 4), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -83,6 +83,20 @@ struct AttnArgs {
   float k_scale;
 };
 
+// Compute units of the current device (queried once per device).
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                   ? n
+                   : 256;
+  }
+  return cus[dev];
+}
+
 // the library's thread-local error text (kvfp8_last_error)
 void set_error(const char* msg);
 void clear_error();

@@ -131,20 +131,24 @@ def kvfp8_attn_workspace_bytes(n_rows: int, n_q_heads: int, head_dim: int, num_s
 
 
 def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Optional[int] = None,
-                   cus: int = 256, seq_lens=None) -> int:
+                   cus: int = 256, seq_lens=None, n_q_heads: Optional[int] = None, q_len: int = 1) -> int:
     """Split count for the split kernel (host-side heuristic).
 
-    Aims for at most two workgroups per compute unit (the split kernel's
-    occupancy) with equal work. All sequences of a call share one split size,
-    set by the longest context and the split count, so a shorter sequence
-    fills fewer splits. With the context lengths known on the host
-    (seq_lens), this returns the largest split count whose non-empty splits,
-    over all sequences and kv-heads, fit in 2 * cus workgroups. Otherwise the
-    keys (total_keys, or batch * max_seq_len) are divided into 2 * cus shares
-    and the longest sequence is split into shares of that size. Splits hold
-    at least 512 keys (unless there is only one); at most 256 splits."""
-    slots = 2 * cus
+    Aims for one round of equal-work workgroups over the compute units: the
+    kernel runs one workgroup per CU when a kv-head has at most 16 query rows
+    (q_len times the GQA group n_q_heads / n_kv_heads; decode, unless the group
+    exceeds 16) and two otherwise. All sequences of a call share one split
+    size, set by the longest context and the split count, so a shorter
+    sequence fills fewer splits. With the context lengths known on the host
+    (seq_lens), this returns the split count with the most non-empty splits,
+    over all sequences and kv-heads, that still fit in those slots (the
+    smallest such count). Otherwise the keys (total_keys, or batch *
+    max_seq_len) are divided into that many shares and the longest sequence is
+    split into shares of that size. Splits hold at least 512 keys (unless there
+    is only one); at most 256 splits."""
     heads = max(1, n_kv_heads)
+    group = (n_q_heads // heads) if n_q_heads else 1
+    slots = (1 if q_len * group <= 16 else 2) * cus
     if seq_lens is not None:
         lens = [int(x) for x in seq_lens]
         lmax = max(lens) if lens else 0

@@ -91,7 +91,8 @@ def test_mtp3_verify_full(K):
     longest = [int(np.argmax(bt.seq_lens)), int(np.argmin(bt.seq_lens))]
     rows = sorted(set(longest + [5]))
     kc, vc = _check_cache_bytes(db, bt, sc, rows=rows)
-    S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens)
+    S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
+                                 n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
     sm = np.float32(1.0 / np.sqrt(bt.head_dim))
     ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S)
     K.poison_partials(ws, bt.total_q, bt.n_q_heads, bt.head_dim, S)
