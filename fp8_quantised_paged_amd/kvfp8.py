@@ -177,8 +177,8 @@ def workspace(n_rows: int, n_q_heads: int, head_dim: int, num_splits: int,
 
 
 def poison_partials(ws: torch.Tensor, n_rows: int, n_q_heads: int, head_dim: int, num_splits: int):
-    """Fill the partials (not the counters) with NaN, so that any partial the
-    reduction reads without it having been written shows up in the output."""
+    """Fill the partials with NaN, so that any partial the reduction uses
+    without it having been written shows up in the output."""
     for t in workspace_views(ws, n_rows, n_q_heads, head_dim, num_splits):
         t.fill_(float("nan"))
 
