@@ -108,6 +108,59 @@ __global__ __launch_bounds__(64 * kWaves) void split_reduce_kernel(
   }
 }
 
+// Few splits (the decode case): one wavefront per (row, head), four per
+// workgroup, and every load of the unit -- m, l and this lane's dims of o for
+// each split -- issued together, so the kernel waits for memory once. The
+// weights and sums are those of split_reduce_kernel; splits with m = -inf get
+// weight zero without their o being multiplied.
+constexpr int kSmallSplits = 8;
+constexpr int kUnitsPerBlock = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kUnitsPerBlock) void split_reduce_small_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_m, const float* __restrict__ ws_l,
+    int64_t n_units, int num_splits, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * kUnitsPerBlock + (threadIdx.x >> 6);
+  if (unit >= n_units) return;  // uniform over the wavefront
+  const float* m = ws_m + unit * num_splits;
+  const float* l = ws_l + unit * num_splits;
+  const float* o = ws_o + unit * (int64_t)num_splits * D + lane * PER;
+  float ms[kSmallSplits], ls[kSmallSplits], v[kSmallSplits][PER];
+#pragma unroll
+  for (int s = 0; s < kSmallSplits; ++s) {
+    const int sc = min(s, num_splits - 1);  // loads stay inside the unit; extra splits get weight zero
+    ms[s] = s < num_splits ? m[sc] : -INFINITY;
+    ls[s] = l[sc];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[s][j] = o[(int64_t)sc * D + j];
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kSmallSplits; ++s) mx = fmaxf(mx, ms[s]);
+  const float ref = (mx == -INFINITY) ? 0.0f : mx;
+  float den = 0.0f;
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kSmallSplits; ++s) {
+    const float w = (ms[s] == -INFINITY) ? 0.0f : __expf(ms[s] - ref);
+    den += (w != 0.0f) ? w * ls[s] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += (w != 0.0f) ? w * v[s][j] : 0.0f;
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  uint16_t* dst = out + unit * D + lane * PER;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const _Float16 h = (_Float16)(den > 0.0f ? acc[j] * inv : 0.0f);
+    dst[j] = __builtin_bit_cast(uint16_t, h);
+  }
+  if (lse != nullptr && lane == 0) lse[unit] = den > 0.0f ? ref + __logf(den) : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_split_reduce(const float* ws_o, const float* ws_m, const float* ws_l,
@@ -116,6 +169,15 @@ hipError_t launch_split_reduce(const float* ws_o, const float* ws_m, const float
                                hipStream_t stream) {
   int64_t units = (int64_t)n_rows * n_q_heads;
   if (units == 0) return hipSuccess;
+  if (num_splits <= kSmallSplits) {
+    dim3 grid((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock));
+    dim3 block(64 * kUnitsPerBlock);
+    if (head_dim == 128)
+      split_reduce_small_kernel<128><<<grid, block, 0, stream>>>(ws_o, ws_m, ws_l, units, num_splits, out, lse);
+    else
+      split_reduce_small_kernel<64><<<grid, block, 0, stream>>>(ws_o, ws_m, ws_l, units, num_splits, out, lse);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)units);
   dim3 block(64 * kWaves);
   if (head_dim == 128)
