@@ -56,9 +56,17 @@ __global__ __launch_bounds__(256) void calib_amax(const uint16_t* __restrict__ x
   } else {
     for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) m = max(m, (uint32_t)(row[i] & 0x7FFFu));
   }
-  // wave reduction, then one atomic per wave
+  // wave reduction, then the block's four wavefronts meet in LDS and one
+  // atomic per block folds the result in (the atomics of one tensor all go to
+  // one address and are served one after another)
+  __shared__ uint32_t wmax[4];
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(acc + t, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (b != 0u) atomicMax(acc + t, b);
+  }
 }
 
 // acc aliases amax_out: read the folded maximum, write amax and scale.
