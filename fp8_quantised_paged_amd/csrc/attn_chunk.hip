@@ -30,12 +30,20 @@ constexpr int kRows = kWaves * kNB * 16;     // rows per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 
+// LDS rows are 256 bytes: 16 chunks of 8 fp16 values, chunk c of row r stored
+// at position c ^ (r % 16). An MFMA operand read (16 rows, lane group g taking
+// chunk 4c + g of row n) then falls on all 64 banks at once with no conflict,
+// where padded rows (272 or 144 bytes) conflict two-way on gfx950.
+// K rows (keys) hold the D dims in order; V^T rows (dims) hold the tile's 64
+// keys with keys 16g + 8u .. +7 in chunk 4u + g.
+constexpr int kRowHalfs = 128;
+
+__device__ __forceinline__ int swz(int chunk, int row) { return 8 * ((chunk ^ row) & 15); }
+
 template <int D>
 struct ChunkLds {
-  static constexpr int KS = D + 8;           // fp16 row stride of K (keys x dims)
-  static constexpr int VS = kTile + 8;       // fp16 row stride of V^T (dims x keys)
-  _Float16 k[3][kTile][KS];
-  _Float16 v[3][D][VS];
+  _Float16 k[3][kTile][kRowHalfs];
+  _Float16 v[3][D][kRowHalfs];
 };
 
 __device__ __forceinline__ float wave_max_groups(float x) {
@@ -147,11 +155,10 @@ __device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const Chunk
       f16x8 a = e4m3x8_to_f16(r.k[j][0], r.k[j][1]);
       f16x8 b = e4m3x8_to_f16(r.k[j][2], r.k[j][3]);
       // key kk is MFMA row m = 4*(kk/16) + kk%4 of M-tile t = (kk/4)%4; storing it
-      // at LDS row 16t + m makes each QK operand read 16 consecutive rows, which
-      // the padded row stride spreads over distinct banks
+      // at LDS row 16t + m makes each QK operand read 16 consecutive rows
       const int row = 16 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
-      *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg]) = a;
-      *reinterpret_cast<f16x8*>(&s.k[buf][row][16 * seg + 8]) = b;
+      *reinterpret_cast<f16x8*>(&s.k[buf][row][swz(2 * seg, row)]) = a;
+      *reinterpret_cast<f16x8*>(&s.k[buf][row][swz(2 * seg + 1, row)]) = b;
     }
   }
 #pragma unroll
@@ -171,8 +178,8 @@ __device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const Chunk
       }
       f16x8 a = e4m3x8_to_f16(w[0], w[1]);
       f16x8 b = e4m3x8_to_f16(w[2], w[3]);
-      *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg]) = a;
-      *reinterpret_cast<f16x8*>(&s.v[buf][d][16 * kseg + 8]) = b;
+      *reinterpret_cast<f16x8*>(&s.v[buf][d][swz(kseg, d)]) = a;      // keys 16 kseg + 0..7: chunk kseg
+      *reinterpret_cast<f16x8*>(&s.v[buf][d][swz(4 + kseg, d)]) = b;  // keys 16 kseg + 8..15: chunk 4 + kseg
     }
   }
 }
@@ -184,10 +191,11 @@ __device__ __forceinline__ void chunk_qk(const ChunkLds<D>& sm, int buf, int n, 
   constexpr int NC = D / 32;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const _Float16* krow = &sm.k[buf][16 * t + n][16 * g];
+    const _Float16* krow = &sm.k[buf][16 * t + n][0];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 64 * (c >> 1) + 8 * (c & 1));
+      // dims 32c + 8g .. +7 (the Q operand holds the same dims)
+      const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + swz(4 * c + g, n));
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         sc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -272,7 +280,7 @@ __device__ __forceinline__ void chunk_pv(const ChunkLds<D>& sm, int buf, int n, 
   for (int blk = 0; blk < NBLK; ++blk) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const f16x8 va = *reinterpret_cast<const f16x8*>(&sm.v[buf][16 * blk + n][16 * g + 8 * u]);
+      const f16x8 va = *reinterpret_cast<const f16x8*>(&sm.v[buf][16 * blk + n][swz(4 * u + g, n)]);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         o[nb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(f16x8, pk[nb][u]),
@@ -332,10 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_chunk_kernel(const AttnArgs 
     if (rr < nrows) {
       const int i = rr / G;
       const int h = kvh * G + rr % G;
-      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
+      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 8 * g;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 64 * (c >> 1) + 8 * (c & 1));
+      for (int c = 0; c < NC; ++c) qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 32 * c);
       lim[nb] = L - T + i + 1;
     } else {
 #pragma unroll
