@@ -212,12 +212,19 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
   const int ntiles = end > start ? (end - start + kTileF - 1) / kTileF : 0;
   const int s_fill_end = (s == itm.n_used - 1) ? S : s + 1;
 
-  if (ntiles == 0 && a.out == nullptr) {
+  // An item with no keys (a sequence of length 0) returns before any K/V load:
+  // its page ids would not name a page. It writes m = -inf and l = 0 for its
+  // split slots, or zero output rows when there is no workspace.
+  if (ntiles == 0) {
     for (int rr = threadIdx.x; rr < nrows; rr += 64 * W) {
-      const int64_t unit = ((int64_t)(q0 + rr / G) * a.n_q_heads + kvh * G + rr % G) * S;
-      for (int s2 = s; s2 < s_fill_end; ++s2) {
-        a.ws_m[unit + s2] = -INFINITY;
-        a.ws_l[unit + s2] = 0.0f;
+      const int64_t row = (int64_t)(q0 + rr / G) * a.n_q_heads + kvh * G + rr % G;
+      if (a.out != nullptr) {
+        for (int d = 0; d < D; d += 8) *reinterpret_cast<u32x4*>(a.out + row * D + d) = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        for (int s2 = s; s2 < s_fill_end; ++s2) {
+          a.ws_m[row * S + s2] = -INFINITY;
+          a.ws_l[row * S + s2] = 0.0f;
+        }
       }
     }
     return;
