@@ -168,8 +168,10 @@ __device__ __forceinline__ void chunk_store(ChunkLds<D>& s, int buf, const Chunk
       const int d = e >> 2;
       const int kseg = e & 3;
       u32x4 w = r.v[j];
-      const int c = L - (t0 + 16 * kseg);  // valid keys among the 16
-      if (c < 16) {
+      // only the tiles reaching past the sequence end need the per-key mask; the
+      // test is uniform over the workgroup, so other tiles skip it entirely
+      if (t0 + kTile > L) {
+        const int c = L - (t0 + 16 * kseg);  // valid keys among the 16
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ci = c - 4 * i;
