@@ -324,6 +324,32 @@ KVFP8_API int32_t paged_attn_e4m3_verify(const uint16_t* q_f16, const int32_t* c
   return run_attention(c, cu_q_lens, total_q, max_q_len, stream);
 }
 
+KVFP8_API int32_t paged_attn_e4m3_verify_append(const uint16_t* q_f16, const uint16_t* k_new, const uint16_t* v_new,
+                                                const int32_t* cu_q_lens, int32_t total_q, int32_t max_q_len,
+                                                uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
+                                                const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                                int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                                int32_t max_pages_per_seq, float k_scale, float v_scale, float sm_scale,
+                                                int32_t num_splits, float* workspace, size_t workspace_bytes,
+                                                uint16_t* out_f16, hipStream_t stream) {
+  AttnCommon c{q_f16, k_cache, v_cache, block_table, seq_lens, batch, n_q_heads, n_kv_heads,
+               head_dim, page_size, max_pages_per_seq, k_scale, v_scale, sm_scale, num_splits,
+               workspace, workspace_bytes, out_f16};
+  if (!cu_q_lens) return fail(KVFP8_INVALID_ARG, "null cu_q_lens");
+  if (total_q < 0) return fail(KVFP8_INVALID_ARG, "negative total_q");
+  if (max_q_len < 1 && total_q > 0) return fail(KVFP8_INVALID_ARG, "max_q_len must be >= 1");
+  int32_t st = check_common(c, total_q);
+  if (st != KVFP8_OK) return st;
+  if ((int64_t)max_q_len * (n_q_heads / n_kv_heads) > kSplitRows)
+    return fail(KVFP8_UNSUPPORTED, "appending takes at most %d query rows per kv-head (max_q_len * group)",
+                kSplitRows);
+  if (total_q > 0 && (!k_new || !v_new)) return fail(KVFP8_INVALID_ARG, "null new-token pointer");
+  if (total_q > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(KVFP8_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  const AppendArgs app{k_new, v_new, k_cache, v_cache};
+  return run_attention(c, cu_q_lens, total_q, max_q_len, stream, &app);
+}
+
 KVFP8_API int32_t paged_attn_f16_decode(const uint16_t* q_f16, const uint16_t* k_cache_f16,
                                         const uint16_t* v_cache_f16, const int32_t* block_table,
                                         const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,

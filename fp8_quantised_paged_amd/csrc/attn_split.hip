@@ -375,27 +375,34 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
     return;
   }
 
-  // ---- append (decode only): the wavefront that will load the tile holding
-  // key L - 1 first quantises the sequence's new token into that slot, exactly
-  // as the cache write does, and waits for its stores before any load of its
-  // own; no other wavefront or workgroup reads that page.
-  if constexpr (NB == 1) {
-    if (a.k_new != nullptr && ntiles > 0 && end == L && wave == (ntiles - 1) % W) {
+  // ---- append: each of the sequence's new tokens (key positions L - T ..
+  // L - 1, this step's query tokens) is quantised into its slot, exactly as
+  // the cache write does, by the wavefront that will load the tile holding it,
+  // which then waits for its stores before any load of its own; no other
+  // wavefront or workgroup reads that tile (tiles and splits start on
+  // multiples of 64 keys, and pages hold at most 64).
+  if (a.k_new != nullptr && ntiles > 0) {
+    const int first_new = max(start, L - T);
+    if (first_new < end) {
       constexpr int PER = D / 64;  // dims per lane
-      const int pos = L - 1;
-      const uint64_t page = (uint32_t)a.block_table[(int64_t)b * a.max_pages + pos / P];
-      const int off = pos % P;
-      const int64_t src = ((int64_t)b * a.n_kv_heads + kvh) * D + PER * lane;
-      uint8_t* kd = a.k_cache_w + ((page * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
-      uint8_t* vd = a.v_cache_w + ((page * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
+      bool wrote = false;
+      for (int pos = first_new; pos < end; ++pos) {
+        if (wave != ((pos - start) / kTile) % W) continue;
+        const uint64_t page = (uint32_t)a.block_table[(int64_t)b * a.max_pages + pos / P];
+        const int off = pos % P;
+        const int64_t src = ((int64_t)(q0 + pos - (L - T)) * a.n_kv_heads + kvh) * D + PER * lane;
+        uint8_t* kd = a.k_cache_w + ((page * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
+        uint8_t* vd = a.v_cache_w + ((page * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const float kx = (float)__builtin_bit_cast(_Float16, a.k_new[src + j]);
-        const float vx = (float)__builtin_bit_cast(_Float16, a.v_new[src + j]);
-        kd[j] = (uint8_t)e4m3_encode(kx / a.k_scale);
-        vd[(int64_t)j * P] = (uint8_t)e4m3_encode(vx / a.v_scale);
+        for (int j = 0; j < PER; ++j) {
+          const float kx = (float)__builtin_bit_cast(_Float16, a.k_new[src + j]);
+          const float vx = (float)__builtin_bit_cast(_Float16, a.v_new[src + j]);
+          kd[j] = (uint8_t)e4m3_encode(kx / a.k_scale);
+          vd[(int64_t)j * P] = (uint8_t)e4m3_encode(vx / a.v_scale);
+        }
+        wrote = true;
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      if (wrote) __builtin_amdgcn_s_waitcnt(0);
     }
   }
 

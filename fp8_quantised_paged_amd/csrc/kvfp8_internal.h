@@ -74,9 +74,10 @@ struct AttnArgs {
   float* ws_m;
   float* ws_l;
   uint16_t* out;  // direct mode (num_splits == 1)
-  // decode with append: the new token of sequence b (key seq_lens[b] - 1) is
-  // quantised into the cache before it is read; nullptr otherwise
-  const uint16_t* k_new;  // [batch][n_kv_heads][head_dim] fp16
+  // with append: the new tokens of sequence b (keys seq_lens[b] - q_len ..
+  // seq_lens[b] - 1, its query rows) are quantised into the cache before they
+  // are read; nullptr otherwise
+  const uint16_t* k_new;  // [query rows][n_kv_heads][head_dim] fp16
   const uint16_t* v_new;
   uint8_t* k_cache_w;  // the same caches, writable
   uint8_t* v_cache_w;

@@ -26,6 +26,7 @@ EXPORTED = (
     "paged_attn_e4m3_decode",
     "paged_attn_e4m3_decode_append",
     "paged_attn_e4m3_verify",
+    "paged_attn_e4m3_verify_append",
     "paged_attn_f16_decode",
     "paged_attn_f16_verify",
     "split_reduce_fp32",
@@ -63,6 +64,8 @@ def _load() -> ctypes.CDLL:
                                                 F32, F32, I32, P, SZ, P, P]),
         "paged_attn_e4m3_verify": (I32, [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                          F32, F32, F32, I32, P, SZ, P, P]),
+        "paged_attn_e4m3_verify_append": (I32, [P, P, P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                                F32, F32, F32, I32, P, SZ, P, P]),
         "paged_attn_f16_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32, P, SZ, P, P]),
         "paged_attn_f16_verify": (I32, [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32,
                                         P, SZ, P, P]),
@@ -332,6 +335,45 @@ def paged_attn_e4m3_verify(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: 
                                        seq_lens.data_ptr(), B, hq, hkv, d, psz, block_table.shape[1],
                                        float(k_scale), float(v_scale), float(sm_scale), int(num_splits),
                                        ws_ptr, ws_bytes, _ptr(out), _stream()), "paged_attn_e4m3_verify")
+    return out
+
+
+def paged_attn_e4m3_verify_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  cu_q_lens: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                  k_scale: float, v_scale: float, sm_scale: float, num_splits: int = 1,
+                                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                                  partials_only: bool = False) -> Optional[torch.Tensor]:
+    """MTP verify with the step's new tokens appended: k_new, v_new fp16 [total_q, Hkv, D] (rows in the
+    order of q) are quantised into key positions seq_lens[b] - q_len + i (through the block table), then
+    attended as paged_attn_e4m3_verify."""
+    _need(q, "q", torch.float16, 3)
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    _need(cu_q_lens, "cu_q_lens", torch.int32, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    total_q, hq, d = q.shape
+    B = seq_lens.shape[0]
+    if cu_q_lens.shape[0] != B + 1:
+        raise ValueError("cu_q_lens must have batch + 1 entries")
+    hkv, psz, _ = _cache_dims(k_cache, v_cache, d)
+    if tuple(k_new.shape) != (total_q, hkv, d) or tuple(v_new.shape) != (total_q, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{total_q}, {hkv}, {d}]")
+    if partials_only:
+        out = None
+    elif out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16, 3)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.paged_attn_e4m3_verify_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cu_q_lens.data_ptr(),
+                                              total_q, int(max_q_len), k_cache.data_ptr(), v_cache.data_ptr(),
+                                              block_table.data_ptr(), seq_lens.data_ptr(), B, hq, hkv, d, psz,
+                                              block_table.shape[1], float(k_scale), float(v_scale), float(sm_scale),
+                                              int(num_splits), ws_ptr, ws_bytes, _ptr(out), _stream()),
+           "paged_attn_e4m3_verify_append")
     return out
 
 

@@ -178,6 +178,27 @@ int32_t paged_attn_e4m3_verify(const uint16_t* q_f16, const int32_t* cu_q_lens, 
                                float v_scale, float sm_scale, int32_t num_splits, float* workspace,
                                size_t workspace_bytes, uint16_t* out_f16, hipStream_t stream);
 
+/* MTP verify step with its new tokens appended ([P1] Purpose and Validation on
+ * 4xV100 TP4: MTP3 verifies the drafted tokens of a step; [P2] Changes: the
+ * quantising cache write). The query tokens of sequence b are its new tokens:
+ * row cu_q_lens[b] + i is key position seq_lens[b] - q_len + i. Their K and V
+ * (k_new, v_new: [total_q][n_kv_heads][head_dim] fp16, 16-byte aligned, rows in
+ * the order of q) are quantised exactly as kv_quant_write does into those
+ * positions (slots found through the block table), then attention runs as
+ * paged_attn_e4m3_verify. The result (cache bytes and output) equals
+ * kv_quant_write of those slots followed by paged_attn_e4m3_verify. Takes at
+ * most 32 query rows per kv-head (max_q_len * group <= 32); larger chunks
+ * return KVFP8_UNSUPPORTED. Other arguments, errors and the workspace as for
+ * paged_attn_e4m3_verify. */
+int32_t paged_attn_e4m3_verify_append(const uint16_t* q_f16, const uint16_t* k_new, const uint16_t* v_new,
+                                      const int32_t* cu_q_lens, int32_t total_q, int32_t max_q_len,
+                                      uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                      int32_t max_pages_per_seq, float k_scale, float v_scale, float sm_scale,
+                                      int32_t num_splits, float* workspace, size_t workspace_bytes,
+                                      uint16_t* out_f16, hipStream_t stream);
+
 /* FP16-cache twins of paged_attn_e4m3_decode and paged_attn_e4m3_verify, for
  * the single-variable comparison of cache formats that the pages make (only
  * kv_cache_dtype differs between the arms: [P1] Validation on 4xV100 TP4).

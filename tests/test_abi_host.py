@@ -168,6 +168,33 @@ def test_decode_append_empty_batch_is_a_noop():
     assert append(b=0, kn=None, vn=None) == kvfp8.OK
 
 
+def verify_append(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, cu=FAKE, tq=8, mq=4, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=32,
+             hkv=4, d=128, p=16, mp=8, ks=0.1, vs=0.1, sm=0.088, s=1, ws=None, wsb=0, out=FAKE)
+    a.update(kw)
+    return L.paged_attn_e4m3_verify_append(a["q"], a["kn"], a["vn"], a["cu"], a["tq"], a["mq"], a["kc"], a["vc"],
+                                           a["bt"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"], a["p"], a["mp"],
+                                           a["ks"], a["vs"], a["sm"], a["s"], a["ws"], a["wsb"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), kvfp8.INVALID_ARG),
+    (dict(vn=None), kvfp8.INVALID_ARG),
+    (dict(vn=MIS), kvfp8.INVALID_ARG),
+    (dict(cu=None), kvfp8.INVALID_ARG),
+    (dict(mq=0), kvfp8.INVALID_ARG),
+    (dict(vs=float("nan")), kvfp8.BAD_SCALE),
+    (dict(mq=5), kvfp8.UNSUPPORTED),  # 5 tokens x 8 heads = 40 rows per kv-head
+    (dict(s=2), kvfp8.WORKSPACE),
+])
+def test_verify_append_rejects(kw, status):
+    assert verify_append(**kw) == status
+
+
+def test_verify_append_empty_is_a_noop():
+    assert verify_append(tq=0, kn=None, vn=None) == kvfp8.OK
+
+
 def verify(**kw):
     a = dict(q=FAKE, cu=FAKE, tq=8, mq=4, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=32, hkv=4, d=128,
              p=16, mp=8, ks=0.1, vs=0.1, sm=0.088, s=1, ws=None, wsb=0, out=FAKE)

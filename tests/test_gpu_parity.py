@@ -228,6 +228,51 @@ def test_decode_append_equals_write_then_decode(K, case, S):
     assert np.array_equal(out.view(np.uint16), sep.view(np.uint16))
 
 
+VERIFY_APPEND_CASES = {
+    # new tokens across a split boundary (keys 126..129 at S = 3) and a tile boundary (keys 62..65),
+    # a sequence made only of new tokens; 32 rows per kv-head (LDS-staged tiles)
+    "edges_g8_p16": lambda: make_batch([130, 66, 4, 300], [4, 4, 4, 3], 32, 4, 128, 16, seed=81),
+    # up to 16 rows per kv-head, pages of 8 and 64
+    "g4_p8_d64": lambda: make_batch([70, 9, 17], [2, 1, 3], 8, 2, 64, 8, seed=82),
+    "g4_p64": lambda: make_batch([700, 64, 129], [4, 2, 3], 16, 4, 128, 64, seed=83),
+    # 32 rows per kv-head with pages of 4 (register tiles, no staging)
+    "g8_p4_d64": lambda: make_batch([100, 257], [4, 2], 32, 4, 64, 4, seed=84),
+}
+
+
+@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("case", list(VERIFY_APPEND_CASES))
+def test_verify_append_equals_write_then_verify(K, case, S):
+    """The fused MTP step writes exactly the bytes kv_quant_write would (every
+    cache byte against the oracle) and returns the separate write-then-verify
+    result bit for bit."""
+    bt = VERIFY_APPEND_CASES[case]()
+    _, sc = oracle_scales(bt)
+    ks, vs, sm = float(sc[0]), float(sc[1]), float(sm_of(bt))
+    db = DeviceBatch(bt)
+    prior, new = dev(bt.prior_rows()), dev(bt.new_token_rows())
+    K.kv_quant_write(db.k[prior].contiguous(), db.v[prior].contiguous(), db.slots[prior].contiguous(), ks, vs,
+                     db.k_cache, db.v_cache)
+    kc_sep, vc_sep = db.k_cache.clone(), db.v_cache.clone()
+    k_new, v_new = db.k[new].contiguous(), db.v[new].contiguous()
+    mq = int(bt.q_lens.max())
+    ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
+    if ws is not None:
+        K.poison_partials(ws, bt.total_q, bt.n_q_heads, bt.head_dim, S)
+    out = K.paged_attn_e4m3_verify_append(db.q, k_new, v_new, db.cu_q, mq, db.k_cache, db.v_cache,
+                                          db.block_table, db.seq_lens, ks, vs, sm, num_splits=S,
+                                          workspace=ws).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    assert np.array_equal(db.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy(), vc)
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm_of(bt))
+    assert_close_attn(out, ref, f"verify append {case} S={S}")
+    K.kv_quant_write(k_new, v_new, db.slots[new].contiguous(), ks, vs, kc_sep, vc_sep)
+    sep = K.paged_attn_e4m3_verify(db.q, db.cu_q, mq, kc_sep, vc_sep, db.block_table, db.seq_lens, ks, vs, sm,
+                                   num_splits=S, workspace=ws).cpu().numpy()
+    assert np.array_equal(out.view(np.uint16), sep.view(np.uint16))
+
+
 VERIFY_CASES = {
     "mtp3_small": lambda: make_batch([1024, 70, 4, 300], [4] * 4, 32, 4, 128, 16, seed=61),
     "ragged_q": lambda: make_batch([50, 9, 200, 3], [1, 2, 4, 3], 32, 4, 128, 16, seed=62),
