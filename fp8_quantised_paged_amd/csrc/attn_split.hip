@@ -2,14 +2,19 @@
 // (sequence, kv-head): decode (1 query token, the GQA group as rows) and MTP
 // verify (a few query tokens with a causal mask among them).
 //
-// Work decomposition: one workgroup per (split, kv-head, sequence); its W
-// wavefronts take interleaved 64-key tiles of the split and merge their
-// online-softmax states through LDS at the end.
+// Work decomposition: one workgroup per (sequence, kv-head, split) item of the
+// work plan (split_plan.h: one split size for the whole batch, the items with
+// keys numbered first); its W wavefronts (8 for a decode grid that fits one
+// round of the compute units, else 4) take interleaved 64-key tiles of the
+// split and merge their online-softmax states through LDS at the end. With
+// new tokens to append (decode or MTP verify), each is quantised into the cache
+// by the wavefront that will load the tile holding it, before its first load.
 //
 // Per 64-key tile a wavefront computes S^T = K Q^T and O^T += V^T P^T with
 // v_mfma_f32_16x16x32_f16:
 //  * QK: A = 16 keys x 32 dims of K (decoded from E4M3 in registers), B = the
-//    same 32 dims x 16 query rows of Q (fp16, held in LDS for the workgroup).
+//    same 32 dims x 16 query rows of Q (fp16; decode re-reads it from LDS every
+//    tile, verify keeps it in registers).
 //    The contraction order over dims is free, so MFMA c takes, in lane group
 //    g (lanes 16g..16g+15), dims 16g + 64*(c/2) + 8*(c%2) + i: each load
 //    instruction then reads 64 contiguous bytes of 16 key rows. The key of
