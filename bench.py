@@ -104,6 +104,7 @@ class Point:
         self.block_table = torch.from_numpy(bt.block_table).to(dev)
         self.seq_lens = torch.from_numpy(bt.seq_lens).to(dev)
         slots = torch.from_numpy(bt.slot_mapping).to(dev)
+        self.slots_all = slots
         new_rows = torch.from_numpy(bt.new_token_rows()).to(dev)
         self.k_new = k_src[new_rows].contiguous()
         self.v_new = v_src[new_rows].contiguous()
@@ -236,6 +237,37 @@ class Point:
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / (launches * replays)
+
+
+    def time_fill(self, k_src, v_src, launches=12, replays=3):
+        """The cache-fill write (every token of the workload in one
+        kv_quant_write launch, as a prefill writes its prompt): average duration
+        from HIP events around graph replays of `launches` back-to-back fills
+        rotated over the point's cache sets. Algorithmic bytes per launch: fp16
+        K and V in, one E4M3 code each out, 8 slot bytes per token."""
+        torch = self.torch
+        n = len(self.sets)
+        launches = max(launches // n, 1) * n
+
+        def fill(i):
+            kc, vc = self.sets[i % n]
+            self.K.kv_quant_write(k_src, v_src, self.slots_all, self.ks, self.vs, kc, vc)
+
+        g = self.capture(fill, launches)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / (launches * replays)
+        tokens = int(k_src.shape[0])
+        nbytes = tokens * self.Hkv * self.D * (2 + 2 + 1 + 1) + 8 * tokens
+        return {"tokens": tokens, "launches": launches * replays, "kernel_us": sec * 1e6,
+                "algorithmic_bytes": nbytes, "gbs": nbytes / sec / 1e9,
+                "frac_of_hbm_peak": nbytes / sec / 1e9 / HBM_PEAK_GBS}
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
@@ -511,6 +543,9 @@ def main():
         else:
             raise SystemExit(f"unknown point {p}")
         pt = Point(K, torch, p, bt, k_src, v_src, calib, S, nsets, f16=p.endswith("_f16"))
+        fill = pt.time_fill(k_src, v_src) if p == "4k" else None
+        if fill is not None:
+            log(f"{p}: cache-fill write {json.dumps(fill)}")
         del k_src, v_src
         torch.cuda.empty_cache()
         log(f"{p}: batch {pt.B} splits {S} kv bytes {pt.kv_bytes}; timing {steps} steps")
@@ -536,6 +571,8 @@ def main():
             "attn_kernel_us": kern * 1e6, "attn_kernel_gbs": pt.alg_bytes / kern / 1e9,
             "graph_replay_matches_eager": same, "cache_sets": nsets,
         }
+        if fill is not None:
+            results[p]["cache_fill_write"] = fill
         log(f"{p}: {json.dumps(results[p])}")
         del pt
         torch.cuda.empty_cache()

@@ -125,6 +125,61 @@ def test_quant_write_bit_exact(K, case):
     assert np.array_equal(db.v_cache.cpu().numpy(), vc)
 
 
+def _slot_pattern(kind, P, num_pages, rng):
+    cap = num_pages * P
+    if kind == "scattered":  # one token per page here and there (decode-like)
+        return rng.permutation(cap)[:300]
+    if kind == "scattered_small":  # a decode step's size
+        return rng.permutation(cap)[:100]
+    if kind == "runs":  # contiguous runs from arbitrary starts, in random order
+        runs, used = [], set()
+        while len(runs) < 12:
+            st, n = int(rng.integers(0, cap - 300)), int(rng.integers(1, 300))
+            if used.isdisjoint(range(st, st + n)):
+                used.update(range(st, st + n))
+                runs.append(np.arange(st, st + n))
+        return np.concatenate(runs)
+    if kind == "runs_with_holes":  # one long run with padding and out-of-range slots in it
+        s = np.arange(5, 5 + 700)
+        s[rng.integers(0, 700, 40)] = -1
+        s[rng.integers(0, 700, 3)] = cap + 7
+        return s
+    # "paged": whole and partial pages in a random page order (a prefill through a block table);
+    # "paged_large": the same over most pages of a larger cache
+    out = []
+    for p in rng.permutation(num_pages)[: (num_pages // 2 if kind == "paged" else num_pages - 8)]:
+        out.append(int(p) * P + np.arange(int(rng.integers(1, P + 1))))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("kind", ["scattered_small", "scattered", "runs", "runs_with_holes", "paged", "paged_large"])
+@pytest.mark.parametrize("D,P", [(128, 4), (128, 16), (128, 64), (64, 8), (64, 32)])
+def test_quant_write_slot_patterns(K, kind, D, P):
+    """The write stores V in runs of consecutive slots, aligned quads and single
+    bytes, with three workgroup shapes chosen by the call's size (up to 256
+    tokens; fewer than about four workgroups per CU; more): every slot pattern
+    and size gives the oracle's cache bytes exactly."""
+    rng = np.random.default_rng([sum(map(ord, kind)), D, P])
+    if kind == "paged_large":  # about 24,000 tokens over 8 kv-heads: the large-call shape
+        num_pages, hkv = 48000 // P + 8, 8
+    else:
+        num_pages, hkv = 3000 // P + 8, 2
+    slots = _slot_pattern(kind, P, num_pages, rng).astype(np.int64)
+    n = slots.shape[0]
+    k = (rng.standard_normal((n, hkv, D)) * 2).astype(np.float16)
+    v = (rng.standard_normal((n, hkv, D)) * 2).astype(np.float16)
+    ks, vs = np.float32(0.02), np.float32(0.015)
+    kc_d = torch.full((num_pages, hkv, P, D), 0x7F, dtype=torch.uint8, device="cuda")
+    vc_d = torch.full((num_pages, hkv, D, P), 0x7F, dtype=torch.uint8, device="cuda")
+    print(f"write {kind} D {D} P {P} tokens {n}", flush=True)
+    K.kv_quant_write(dev(k), dev(v), dev(slots), float(ks), float(vs), kc_d, vc_d)
+    from oracle import new_caches, quant_write
+    kc, vc = new_caches(num_pages, hkv, P, D)
+    quant_write(k, v, slots, ks, vs, kc, vc)
+    assert np.array_equal(kc_d.cpu().numpy(), kc)
+    assert np.array_equal(vc_d.cpu().numpy(), vc)
+
+
 def test_quant_write_skips_padding_and_saturates(K):
     bt = make_batch([40], [1], 8, 2, 64, 16, seed=45)
     bt.k[7, 0, :8] = np.float16(60000.0)  # far beyond 448 * scale: saturates
