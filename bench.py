@@ -150,8 +150,8 @@ class Point:
                                           self.vs, self.sm, **kw)
 
     def attend(self, i):
-        """The attention kernel alone (partials only)."""
-        self._call(i, None)
+        """The attention kernel alone (partials only; unsplit calls write out)."""
+        self._call(i, self.out if self.S == 1 else None)
 
     def step(self, i):
         """Write kernel, then attention (and the reduce when split). The fp16
