@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvfp8.so")
 SOURCES = ["api.cpp", "scale_overlay.cpp", "calibrate.hip", "quant_write.hip", "attn_split.hip", "attn_split_f16.hip",
-           "attn_chunk.hip", "split_reduce.hip"]
+           "attn_chunk.hip", "split_reduce.hip", "check_args.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

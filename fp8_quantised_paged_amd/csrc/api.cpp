@@ -418,3 +418,39 @@ KVFP8_API int32_t kvfp8_e4m3_decode_f32(const uint8_t* codes, float* x, int64_t 
   if (!x || !codes) return fail(KVFP8_INVALID_ARG, "null pointer");
   return hip_status(kvfp8::launch_decode(codes, x, n, stream), "decode launch");
 }
+
+KVFP8_API int32_t kvfp8_check_paged_args(const int32_t* block_table, const int32_t* seq_lens,
+                                         const int32_t* cu_q_lens, int32_t batch, int32_t max_pages_per_seq,
+                                         int32_t page_size, int64_t num_pages, int32_t total_q, int32_t max_q_len,
+                                         int32_t* result, hipStream_t stream) {
+  if (batch < 0) return fail(KVFP8_INVALID_ARG, "negative batch");
+  if (max_pages_per_seq <= 0 || page_size <= 0 || num_pages < 0)
+    return fail(KVFP8_INVALID_ARG, "max_pages_per_seq and page_size must be positive, num_pages non-negative");
+  if (cu_q_lens && (total_q < 0 || max_q_len < 0)) return fail(KVFP8_INVALID_ARG, "negative total_q or max_q_len");
+  if (batch == 0) return ok();
+  if (!block_table || !seq_lens || !result) return fail(KVFP8_INVALID_ARG, "null pointer");
+  if ((reinterpret_cast<uintptr_t>(result) & 3u) != 0) return fail(KVFP8_INVALID_ARG, "result must be 4-byte aligned");
+  hipError_t e = kvfp8::launch_check_paged_args(block_table, seq_lens, cu_q_lens, batch, max_pages_per_seq,
+                                                page_size, num_pages, total_q, max_q_len, result, stream);
+  if (e != hipSuccess) return hip_status(e, "argument check launch");
+  int32_t r[4] = {0, 0, 0, 0};
+  e = hipMemcpyAsync(r, result, sizeof(r), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_status(e, "argument check readback");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "argument check synchronise");
+  if (r[0] == 0) return ok();
+  char detail[320];
+  int len = 0;
+  detail[0] = '\0';
+  if (r[0] & kvfp8::kCheckBadSeqLen)
+    len += snprintf(detail + len, sizeof(detail) - (size_t)len,
+                    "seq_lens outside [0, max_pages_per_seq * page_size] (first at sequence %d); ", r[1]);
+  if ((r[0] & kvfp8::kCheckBadQueries) && len < (int)sizeof(detail))
+    len += snprintf(detail + len, sizeof(detail) - (size_t)len,
+                    "query rows outside [0, max_q_len], above seq_lens, or cu_q_lens not starting at 0 / "
+                    "ending at total_q (first at sequence %d); ", r[2]);
+  if ((r[0] & kvfp8::kCheckBadPage) && len < (int)sizeof(detail))
+    snprintf(detail + len, sizeof(detail) - (size_t)len,
+             "block-table entry outside [0, num_pages) (first at sequence %d); ", r[3]);
+  return fail(KVFP8_INVALID_ARG, "%s", detail);
+}

@@ -118,6 +118,14 @@ hipError_t launch_split_reduce(const float* ws_o, const float* ws_m, const float
                                int32_t n_rows, int32_t n_q_heads, int32_t head_dim,
                                int32_t num_splits, uint16_t* out, float* lse,
                                hipStream_t stream);
+// Device-side check of the attention calls' caller contract; result: int32[4]
+// (rule bits, then the first offending sequence per rule).
+constexpr int32_t kCheckBadSeqLen = 1;   // seq_lens[b] < 0 or > max_pages * page_size
+constexpr int32_t kCheckBadQueries = 2;  // q_len out of [0, max_q_len], above seq_lens[b], or bad cu_q_lens ends
+constexpr int32_t kCheckBadPage = 4;     // a block-table entry of a page holding keys outside [0, num_pages)
+hipError_t launch_check_paged_args(const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_q_lens,
+                                   int32_t batch, int32_t max_pages, int32_t page_size, int64_t num_pages,
+                                   int32_t total_q, int32_t max_q_len, int32_t* result, hipStream_t stream);
 hipError_t launch_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 hipError_t launch_decode(const uint8_t* codes, float* x, int64_t n, hipStream_t stream);
 

@@ -35,6 +35,7 @@ EXPORTED = (
     "kvfp8_last_error",
     "kvfp8_e4m3_encode_f32",
     "kvfp8_e4m3_decode_f32",
+    "kvfp8_check_paged_args",
     "kvfp8_scale_overlay_write",
     "kvfp8_scale_overlay_read",
 )
@@ -71,6 +72,7 @@ def _load() -> ctypes.CDLL:
                                         P, SZ, P, P]),
         "split_reduce_fp32": (I32, [P, P, P, I32, I32, I32, I32, P, P, P]),
         "kvfp8_e4m3_encode_f32": (I32, [P, P, I64, P]),
+        "kvfp8_check_paged_args": (I32, [P, P, P, I32, I32, I32, I64, I32, I32, P, P]),
         "kvfp8_e4m3_decode_f32": (I32, [P, P, I64, P]),
         "kvfp8_scale_overlay_write": (I32, [ctypes.c_char_p, ctypes.c_char_p, I32, P, P]),
         "kvfp8_scale_overlay_read": (I32, [ctypes.c_char_p, ctypes.c_char_p, I32, P, P]),
@@ -463,6 +465,30 @@ def split_reduce_fp32(ws_o: torch.Tensor, ws_m: torch.Tensor, ws_l: torch.Tensor
     _check(_lib.split_reduce_fp32(ws_o.data_ptr(), ws_m.data_ptr(), ws_l.data_ptr(), R, hq, d, S,
                                   out.data_ptr(), _ptr(lse), _stream()), "split_reduce_fp32")
     return (out, lse) if (with_lse or lse is not None) else out
+
+
+def kvfp8_check_paged_args(block_table: torch.Tensor, seq_lens: torch.Tensor, page_size: int, num_pages: int,
+                           cu_q_lens: Optional[torch.Tensor] = None, total_q: int = 0, max_q_len: int = 0,
+                           result: Optional[torch.Tensor] = None) -> None:
+    """Device check of the attention calls' caller contract (block table, context
+    lengths, query offsets); raises KVFP8Error (KVFP8_INVALID_ARG) naming every
+    broken rule. block_table int32 [B, max_pages]; seq_lens int32 [B]; cu_q_lens
+    int32 [B+1] for verify (None: decode) with total_q, the number of query
+    rows, and max_q_len as passed to the verify call. Synchronous."""
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, max_pages = block_table.shape
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must have one entry per block-table row")
+    if cu_q_lens is not None:
+        _need(cu_q_lens, "cu_q_lens", torch.int32, 1)
+        if cu_q_lens.shape[0] != B + 1:
+            raise ValueError("cu_q_lens must have batch + 1 entries")
+    if result is None:
+        result = torch.empty(4, dtype=torch.int32, device=block_table.device)
+    _check(_lib.kvfp8_check_paged_args(block_table.data_ptr(), seq_lens.data_ptr(), _ptr(cu_q_lens), B, max_pages,
+                                       int(page_size), int(num_pages), int(total_q), int(max_q_len), result.data_ptr(),
+                                       _stream()), "kvfp8_check_paged_args")
 
 
 def kvfp8_e4m3_encode_f32(x: torch.Tensor) -> torch.Tensor:

@@ -37,7 +37,8 @@
  * data): block-table entries of pages that hold keys are valid page ids below
  * num_pages; 1 <= q_len <= seq_lens[b] <= max_pages_per_seq * page_size; the
  * slots passed to kv_quant_write are distinct. Entries of the block table past
- * a sequence's last page are never read.
+ * a sequence's last page are never read. kvfp8_check_paged_args checks the
+ * block-table and length parts on the device.
  */
 #ifndef KVFP8_H
 #define KVFP8_H
@@ -235,6 +236,28 @@ int32_t paged_attn_f16_verify(const uint16_t* q_f16, const int32_t* cu_q_lens, i
 int32_t split_reduce_fp32(const float* ws_o, const float* ws_m, const float* ws_l, int32_t n_rows,
                           int32_t n_q_heads, int32_t head_dim, int32_t num_splits, uint16_t* out_f16,
                           float* lse_out, hipStream_t stream);
+
+/* Check of the device-side caller contract above ([P2] Purpose: unsupported
+ * combinations fail closed). The attention calls cannot see their block table,
+ * context lengths and query offsets from the host; a caller that cannot vouch
+ * for them (a debug build, a fuzzer, a new scheduler) runs this check first with
+ * the same arguments. block_table: [batch][max_pages_per_seq] int32;
+ * seq_lens: [batch] int32; cu_q_lens: [batch+1] int32 for verify, or NULL for
+ * decode (one query row per sequence); num_pages: pages in the caches;
+ * total_q, max_q_len: as for paged_attn_e4m3_verify (ignored without
+ * cu_q_lens); result: int32[4] device scratch owned by the caller, overwritten.
+ * Returns KVFP8_OK when for every sequence b, with q_len = 1 (decode) or
+ * cu_q_lens[b+1] - cu_q_lens[b] (verify):
+ *   0 <= seq_lens[b] <= max_pages_per_seq * page_size,
+ *   0 <= q_len <= max_q_len (verify), q_len <= seq_lens[b],
+ *   cu_q_lens[0] == 0 and cu_q_lens[batch] == total_q (verify),
+ *   0 <= block_table[b][i] < num_pages for i < ceil(seq_lens[b] / page_size);
+ * otherwise KVFP8_INVALID_ARG, and kvfp8_last_error() names each broken rule
+ * with the first sequence that breaks it. Synchronous (waits on `stream` for
+ * its result); not capturable in a graph. batch == 0 is a no-op. */
+int32_t kvfp8_check_paged_args(const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_q_lens,
+                               int32_t batch, int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                               int32_t total_q, int32_t max_q_len, int32_t* result, hipStream_t stream);
 
 /* Device E4M3 codec exposed for testing the conversions the kernels use.
  * kvfp8_e4m3_encode_f32: codes[i] = E4M3(x[i]) with the rounding and

@@ -259,3 +259,27 @@ def test_codec_helpers_reject():
     assert L.kvfp8_e4m3_encode_f32(FAKE, FAKE, -1, None) == kvfp8.INVALID_ARG
     assert L.kvfp8_e4m3_decode_f32(None, FAKE, 5, None) == kvfp8.INVALID_ARG
     assert L.kvfp8_e4m3_decode_f32(FAKE, FAKE, 0, None) == kvfp8.OK
+
+
+def check_args(bt=FAKE, sl=FAKE, cu=None, b=2, mp=8, p=16, npg=64, tq=0, mq=0, res=FAKE):
+    return L.kvfp8_check_paged_args(bt, sl, cu, b, mp, p, npg, tq, mq, res, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(b=-1), kvfp8.INVALID_ARG),
+    (dict(mp=0), kvfp8.INVALID_ARG),
+    (dict(p=0), kvfp8.INVALID_ARG),
+    (dict(npg=-1), kvfp8.INVALID_ARG),
+    (dict(cu=FAKE, tq=-1), kvfp8.INVALID_ARG),
+    (dict(cu=FAKE, mq=-1), kvfp8.INVALID_ARG),
+    (dict(bt=None), kvfp8.INVALID_ARG),
+    (dict(sl=None), kvfp8.INVALID_ARG),
+    (dict(res=None), kvfp8.INVALID_ARG),
+    (dict(res=FAKE + 2), kvfp8.INVALID_ARG),
+])
+def test_check_paged_args_rejects(kw, status):
+    assert check_args(**kw) == status
+
+
+def test_check_paged_args_empty_batch_is_a_noop():
+    assert check_args(b=0, bt=None, sl=None, res=None) == kvfp8.OK
