@@ -239,6 +239,79 @@ class Point:
         return e0.elapsed_time(e1) / 1e3 / (launches * replays)
 
 
+    def _time_graph(self, fn, launches, replays=5):
+        """Average duration of fn(i) from HIP events around `replays` replays of
+        a graph of `launches` back-to-back calls."""
+        torch = self.torch
+        g = self.capture(fn, launches)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / (launches * replays)
+
+    def time_reduce(self, launches=60):
+        """The split reduce on its own (the partials of the last attention call
+        stay in the workspace)."""
+        if self.S == 1:
+            return None
+        self._call(0, None)
+        return self._time_graph(lambda i: self.K.split_reduce_fp32(self.ws_o, self.ws_m, self.ws_l, out=self.out),
+                                launches)
+
+    def saturated_codes(self):
+        """Cache codes at +-448 (0x7E / 0xFE) over the workload's slots, K and V."""
+        if self.f16:
+            return None
+        kc, vc = self.sets[0]
+        pg = self.slots_all // self.P
+        off = self.slots_all % self.P
+        k = kc[pg, :, off, :]
+        v = vc[pg, :, :, off]
+        sat = int(((k & 0x7F) == 0x7E).sum().item() + ((v & 0x7F) == 0x7E).sum().item())
+        return {"saturated": sat, "codes": int(k.numel() + v.numel()),
+                "fraction": sat / float(k.numel() + v.numel())}
+
+    def verify_flops(self):
+        """4 * head_dim flops per visible (query token, key) pair and query head."""
+        pairs = sum(causal_pairs(int(L), int(T)) for L, T in zip(self.bt.seq_lens, self.bt.q_lens))
+        return 4 * self.D * self.Hq * pairs
+
+    def time_buckets(self, launches=12):
+        """The verify kernel on the sequences of each context length alone (the
+        same pages, queries and cache sets), with its own split count."""
+        torch, K, bt = self.torch, self.K, self.bt
+        out = {}
+        lens = bt.seq_lens.astype(np.int64)
+        for L in sorted(set(int(x) for x in lens)):
+            idx = np.nonzero(lens == L)[0]
+            rows = np.concatenate([np.arange(bt.cu_q_lens[b], bt.cu_q_lens[b + 1]) for b in idx])
+            ql = bt.q_lens[idx]
+            cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)).cuda()
+            q = self.q[torch.from_numpy(rows).cuda()].contiguous()
+            btab = self.block_table[torch.from_numpy(idx).cuda()].contiguous()
+            sl = self.seq_lens[torch.from_numpy(idx).cuda()].contiguous()
+            S = K.default_splits(len(idx), self.Hkv, L, seq_lens=lens[idx], n_q_heads=self.Hq, q_len=int(ql.max()))
+            ws = K.workspace(len(rows), self.Hq, self.D, S)
+            o = torch.empty_like(q)
+            n = len(self.sets)
+
+            def call(i, q=q, cu=cu, btab=btab, sl=sl, S=S, ws=ws, o=o, mq=int(ql.max())):
+                kc, vc = self.sets[i % n]
+                kw = dict(num_splits=S, workspace=ws)
+                kw.update(partials_only=True) if S > 1 else kw.update(out=o)
+                K.paged_attn_e4m3_verify(q, cu, mq, kc, vc, btab, sl, self.ks, self.vs, self.sm, **kw)
+
+            sec = self._time_graph(call, max(launches // n, 1) * n)
+            kv = int(L) * len(idx) * self.Hkv * self.D * 2
+            out[str(L)] = {"sequences": int(len(idx)), "query_rows": int(len(rows)), "num_splits": int(S),
+                           "kernel_us": sec * 1e6, "kv_gbs": kv / sec / 1e9}
+        return out
+
     def time_fill(self, k_src, v_src, launches=12, replays=3):
         """The cache-fill write (every token of the workload in one
         kv_quant_write launch, as a prefill writes its prompt): average duration
@@ -573,6 +646,17 @@ def main():
         }
         if fill is not None:
             results[p]["cache_fill_write"] = fill
+        red = pt.time_reduce()
+        if red is not None:
+            results[p]["reduce_us"] = red * 1e6
+        sat = pt.saturated_codes()
+        if sat is not None:
+            results[p]["saturated_codes"] = sat
+        if p == "mtp3":
+            fl = pt.verify_flops()
+            results[p]["mfma_tflops"] = fl / kern / 1e12
+            results[p]["mfma_util"] = fl / kern / 1e12 / MFMA_F16_PEAK_TFLOPS
+            results[p]["buckets"] = pt.time_buckets()
         log(f"{p}: {json.dumps(results[p])}")
         del pt
         torch.cuda.empty_cache()
