@@ -64,6 +64,9 @@ def test_random_plan_e4m3_and_f16(K, seed):
     # E4M3: cache written by the library, oracle over its own quantised cache
     _, sc = oracle_scales(bt)
     db = DeviceBatch(bt)
+    # the generated tables meet the attention calls' device-side contract
+    K.kvfp8_check_paged_args(db.block_table, db.seq_lens, bt.page_size, bt.num_pages,
+                             db.cu_q if verify else None, bt.total_q, int(bt.q_lens.max()))
     K.kv_quant_write(db.k, db.v, db.slots, float(sc[0]), float(sc[1]), db.k_cache, db.v_cache)
     kc, vc = oracle_caches(bt, sc[0], sc[1])
     assert np.array_equal(db.k_cache.cpu().numpy(), kc) and np.array_equal(db.v_cache.cpu().numpy(), vc)
