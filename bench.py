@@ -482,26 +482,33 @@ def cpu_baseline(seconds_target=10.0):
 COPY_BYTES = 1 << 30
 
 
-def counter_pass(K, torch, make_config):
+def counter_pass(K, torch, make_config, point="4k"):
     """Eager, unprofiled-timing launches for `rocprofv3 --pmc` runs. The copy
     reads and writes exactly COPY_BYTES, so its FETCH_SIZE / WRITE_SIZE readings
-    give the scale from counter units to bytes."""
+    give the scale from counter units to bytes. Then 12 attention launches of
+    the 4k decode point (or the MTP3 verify point)."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(3)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    bt = make_config(2)
+    bt = make_config(2 if point == "4k" else 3)
     k_src = torch.from_numpy(bt.k).cuda()
     v_src = torch.from_numpy(bt.v).cuda()
     calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
-    S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)
-    pt = Point(K, torch, "4k", bt, k_src, v_src, calib, S, 6)
+    if point == "4k":
+        S, nsets = K.default_splits(bt.batch, bt.n_kv_heads, 4096), 6
+    else:
+        S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
+                             n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
+        nsets = 2
+    pt = Point(K, torch, point, bt, k_src, v_src, calib, S, nsets)
     for i in range(12):
         pt.attend(i)
     torch.cuda.synchronize()
-    log(f"counter pass: copy {COPY_BYTES} B x3, 12 attention launches (splits {S})")
+    log(f"counter pass: copy {COPY_BYTES} B x3, 12 {point} attention launches (splits {S}, "
+        f"algorithmic bytes {pt.alg_bytes})")
 
 
 def main():
@@ -516,6 +523,8 @@ def main():
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager launches for hardware-counter runs: a 1 GiB device copy "
                          "(reference for the byte counters), then 4k decode attention launches")
+    ap.add_argument("--counter-point", default="4k", choices=("4k", "mtp3"),
+                    help="workload of the counter pass's attention launches")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the library runs on one GPU)",
@@ -529,7 +538,7 @@ def main():
 
     torch.cuda.set_device(0)
     if args.counter_pass:
-        counter_pass(K, torch, make_config)
+        counter_pass(K, torch, make_config, args.counter_point)
         return
     points = [p for p in args.points.split(",") if p]
     results = {}
