@@ -6,7 +6,8 @@
  * memory and keeps no state besides a thread-local error string: the caller
  * owns every buffer. Work is enqueued on the caller's HIP stream and the calls
  * do not synchronise, except kv_calibrate_amax, which is an offline call and
- * waits for its own result. Every call validates its arguments on the host
+ * waits for its own result, and kvfp8_check_paged_args, a debug-time check
+ * that does the same. Every call validates its arguments on the host
  * before touching the GPU and returns a kvfp8_status; on any non-zero status
  * nothing has been launched (except where stated for kv_calibrate_amax).
  *
