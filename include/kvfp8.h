@@ -9,7 +9,8 @@
  * waits for its own result, and kvfp8_check_paged_args, a debug-time check
  * that does the same. Every call validates its arguments on the host
  * before touching the GPU and returns a kvfp8_status; on any non-zero status
- * nothing has been launched (except where stated for kv_calibrate_amax).
+ * nothing has been launched (except for kv_calibrate_amax and
+ * kvfp8_check_paged_args, whose statuses report what their kernels found).
  *
  * The method is described by three pull-request pages:
  *   [P1] "[Model][SM70] Calibrated E4M3 KV cache for Qwen4Exp QSA with MTP"
