@@ -8,8 +8,6 @@
 //   <layer> <k_scale> <v_scale>      (n lines, layers 0 .. n-1 each once, any order)
 // Scales are written as C99 hexadecimal floats, so a read returns the written
 // fp32 values bit for bit.
-#include <hip/hip_runtime.h>
-
 #include <cerrno>
 #include <cmath>
 #include <cfloat>
@@ -21,7 +19,13 @@
 #include <vector>
 
 #include "kvfp8.h"
-#include "kvfp8_internal.h"
+
+// Host-only code (no HIP calls): it also builds with a plain host compiler,
+// which is how the sanitizer test builds it.
+namespace kvfp8 {
+void set_error(const char* msg);  // the library's thread-local error text
+void clear_error();
+}  // namespace kvfp8
 
 #define KVFP8_API extern "C" __attribute__((visibility("default")))
 
