@@ -516,7 +516,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed,4k_p4,4k_f16,mtp3_f16")
+    ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed,4k_p4,4k_tp4,4k_f16,mtp3_f16")
     ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-launches", type=int, default=60)
@@ -561,6 +561,19 @@ def main():
             calib = cal.view(2, -1)
             S = K.default_splits(bt.batch, bt.n_kv_heads, 32768)
             nsets, steps = 2, max(10, args.steps // 3)
+        elif p == "4k_tp4":
+            # one GPU's share of the 4k decode under four-way head parallelism: one kv-head and its
+            # 8 query heads of every sequence (the other kv-heads live on the other GPUs)
+            from synth import make_batch
+            bt = make_batch([4096] * 32, [1] * 32, 8, 1, 128, 16, seed=20260002, name="decode_4k_tp4_share",
+                            calib_tokens=2048, values=False)
+            total = int(bt.cu_seq_lens[-1])
+            k_src = normal_kv(total, 1, 128, bt.seed * 10 + 1)
+            v_src = normal_kv(total, 1, 128, bt.seed * 10 + 2)
+            cal = normal_kv(2 * 2048, 1, 128, bt.seed * 10 + 3)
+            calib = cal.view(2, -1)
+            S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)
+            nsets, steps = 12, args.steps
         elif p == "4k_p4":
             # derived: the 4k decode shape with the pages' grouped page-size-4 layout
             bt = make_config(2, values=False, page_size_override=4)

@@ -50,7 +50,9 @@ __global__ __launch_bounds__(kCheckThreads) void check_paged_args_kernel(
         bad_q = ql < 0 || ql > max_q_len || (b == 0 && c0 != 0) || (b == batch - 1 && c1 != total_q);
       }
       const bool bad_len = L < 0 || (int64_t)L > cap;
-      if (!bad_len && !bad_q && ql > L) bad_q = true;  // a query row would sit before key 0
+      // a verify row would sit before key 0 (a decode row over no keys is allowed:
+      // its output is zero, its partials empty)
+      if (cu_q_lens != nullptr && !bad_len && !bad_q && ql > L) bad_q = true;
       if (bad_len) {
         atomicOr(&s_bits, kCheckBadSeqLen);
         atomicMin(&s_first[0], b);

@@ -37,7 +37,9 @@
  *
  * Caller contract that the host cannot check without a synchronisation (device
  * data): block-table entries of pages that hold keys are valid page ids below
- * num_pages; 1 <= q_len <= seq_lens[b] <= max_pages_per_seq * page_size; the
+ * num_pages; seq_lens[b] <= max_pages_per_seq * page_size, and for verify
+ * q_len <= seq_lens[b] (a decode sequence may have no keys: its output is zero
+ * and its partials empty, as for a context shard holding none of its pages); the
  * slots passed to kv_quant_write are distinct. Entries of the block table past
  * a sequence's last page are never read. kvfp8_check_paged_args checks the
  * block-table and length parts on the device.
@@ -118,7 +120,8 @@ int32_t kv_quant_write(const uint16_t* k_f16, const uint16_t* v_f16, const int64
 /* Decode attention, one query token per sequence ([P2] Changes: grouped-page
  * decode and split routes over the E4M3 cache). q_f16: [batch][n_q_heads]
  * [head_dim] fp16; block_table: [batch][max_pages_per_seq] int32; seq_lens:
- * [batch] int32 (>= 1). out_f16: [batch][n_q_heads][head_dim] fp16.
+ * [batch] int32 (>= 0; a sequence with no keys gets out = 0 and empty
+ * partials). out_f16: [batch][n_q_heads][head_dim] fp16.
  * num_splits >= 1 splits the keys of every sequence into ranges of one size
  * for the whole call, C = ceil(L_max / (64 * num_splits)) * 64 keys with L_max
  * the longest context of the batch: split s covers keys [s*C, min((s+1)*C, L)),
@@ -248,10 +251,10 @@ int32_t split_reduce_fp32(const float* ws_o, const float* ws_m, const float* ws_
  * decode (one query row per sequence); num_pages: pages in the caches;
  * total_q, max_q_len: as for paged_attn_e4m3_verify (ignored without
  * cu_q_lens); result: int32[4] device scratch owned by the caller, overwritten.
- * Returns KVFP8_OK when for every sequence b, with q_len = 1 (decode) or
+ * Returns KVFP8_OK when for every sequence b, with q_len =
  * cu_q_lens[b+1] - cu_q_lens[b] (verify):
  *   0 <= seq_lens[b] <= max_pages_per_seq * page_size,
- *   0 <= q_len <= max_q_len (verify), q_len <= seq_lens[b],
+ *   0 <= q_len <= max_q_len and q_len <= seq_lens[b] (verify),
  *   cu_q_lens[0] == 0 and cu_q_lens[batch] == total_q (verify),
  *   0 <= block_table[b][i] < num_pages for i < ceil(seq_lens[b] / page_size);
  * otherwise KVFP8_INVALID_ARG, and kvfp8_last_error() names each broken rule
