@@ -9,7 +9,7 @@ namespace {
 
 constexpr int kCheckThreads = 256;
 
-// result[0]: rule bits (kBadSeqLen | kBadQueries | kBadPage); result[1..3]: the
+// result[0]: rule bits (kCheckBadSeqLen, kCheckBadQueries, kCheckBadPage); result[1..3]: the
 // lowest offending sequence of each rule (INT32_MAX when none).
 __global__ void check_init_kernel(int32_t* result) {
   if (threadIdx.x == 0) {
