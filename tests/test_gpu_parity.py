@@ -659,3 +659,55 @@ def test_graph_replays_match_eager(K):
         step()  # and an eager call sharing the workspace
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+def test_graph_replay_follows_changing_lengths(K):
+    """One captured split decode replayed while the context lengths and queries
+    change in place between replays (the longest context too, so the split size
+    and the work plan change): the work plan is derived on the device from the
+    lengths, so every replay must equal an eager call on the same inputs bit for
+    bit and match the oracle."""
+    bt = make_batch([2000, 2000, 2000, 2000, 2000], [1] * 5, 32, 4, 128, 16, seed=103)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    sm = float(sm_of(bt))
+    S = 6
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
+    out = torch.empty_like(db.q)
+    seq_lens = db.seq_lens.clone()
+    q = db.q.clone()
+
+    def step():
+        K.paged_attn_e4m3_decode(q, db.k_cache, db.v_cache, db.block_table, seq_lens, float(sc[0]), float(sc[1]),
+                                 sm, num_splits=S, workspace=ws, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(104)
+    for rep, lens in enumerate(([2000, 1, 700, 1999, 64], [5, 9, 3, 1, 2], [1500, 1500, 1500, 1500, 1500],
+                                [64, 128, 2000, 65, 63])):
+        lens = np.asarray(lens, np.int32)
+        qn = rng.standard_normal(bt.q.shape).astype(np.float16)
+        seq_lens.copy_(torch.from_numpy(lens))
+        q.copy_(torch.from_numpy(qn))
+        out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(replayed, out), f"replay {rep} differs from the eager call"
+        cu = np.arange(bt.batch + 1, dtype=np.int32)
+        ref, _ = paged_attention(qn, kc, vc, bt.block_table, lens, cu, sc[0], sc[1], sm)
+        assert_close_attn(replayed.cpu().numpy(), ref, f"replay {rep}")
