@@ -711,3 +711,67 @@ def test_graph_replay_follows_changing_lengths(K):
         cu = np.arange(bt.batch + 1, dtype=np.int32)
         ref, _ = paged_attention(qn, kc, vc, bt.block_table, lens, cu, sc[0], sc[1], sm)
         assert_close_attn(replayed.cpu().numpy(), ref, f"replay {rep}")
+
+
+def test_graph_replay_verify_append_follows_lengths(K):
+    """A captured MTP verify step with its new tokens appended, replayed while
+    the context lengths (and so the new tokens' positions, the split size and
+    the work plan) and the queries change in place between replays. The new
+    tokens are the ones already cached at those positions, so the appends are
+    idempotent and the cache stays the oracle's; every replay equals an eager
+    call bit for bit and matches the oracle."""
+    B, T = 4, 4
+    bt = make_batch([3000] * B, [T] * B, 32, 4, 128, 16, seed=105)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    sm = float(sm_of(bt))
+    S = 6
+    rows = B * T
+    ws = K.workspace(rows, bt.n_q_heads, bt.head_dim, S)
+    out = torch.empty_like(db.q)
+    seq_lens = db.seq_lens.clone()
+    q = db.q.clone()
+    k_new = torch.empty((rows, bt.n_kv_heads, bt.head_dim), dtype=torch.float16, device="cuda")
+    v_new = torch.empty_like(k_new)
+
+    def step():
+        K.paged_attn_e4m3_verify_append(q, k_new, v_new, db.cu_q, T, db.k_cache, db.v_cache, db.block_table,
+                                        seq_lens, float(sc[0]), float(sc[1]), sm, num_splits=S, workspace=ws,
+                                        out=out)
+
+    def set_inputs(lens, qn):
+        tok = np.concatenate([bt.cu_seq_lens[b] + np.arange(L - T, L) for b, L in enumerate(lens)])
+        k_new.copy_(torch.from_numpy(bt.k[tok]))
+        v_new.copy_(torch.from_numpy(bt.v[tok]))
+        seq_lens.copy_(torch.from_numpy(np.asarray(lens, np.int32)))
+        q.copy_(torch.from_numpy(qn))
+
+    rng = np.random.default_rng(106)
+    set_inputs([3000] * B, bt.q)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep, lens in enumerate(([3000, 4, 1029, 64], [700, 701, 702, 703], [4, 4, 4, 2999], [1234, 3000, 17, 65])):
+        qn = rng.standard_normal(bt.q.shape).astype(np.float16)
+        set_inputs(lens, qn)
+        out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(replayed, out), f"replay {rep} differs from the eager call"
+        assert np.array_equal(db.k_cache.cpu().numpy(), kc) and np.array_equal(db.v_cache.cpu().numpy(), vc)
+        ref, _ = paged_attention(qn, kc, vc, bt.block_table, np.asarray(lens, np.int32), bt.cu_q_lens, sc[0], sc[1],
+                                 sm)
+        assert_close_attn(replayed.cpu().numpy(), ref, f"replay {rep}")
