@@ -775,3 +775,51 @@ def test_graph_replay_verify_append_follows_lengths(K):
         ref, _ = paged_attention(qn, kc, vc, bt.block_table, np.asarray(lens, np.int32), bt.cu_q_lens, sc[0], sc[1],
                                  sm)
         assert_close_attn(replayed.cpu().numpy(), ref, f"replay {rep}")
+
+
+def test_graph_replay_chunk_follows_lengths(K):
+    """A captured prefill chunk (the query-tiled chunk kernel: 40 tokens x 8
+    heads per kv-head) replayed while the prior context length and the queries
+    change in place: every replay equals an eager call bit for bit and matches
+    the oracle."""
+    T = 40
+    bt = make_batch([2000, 2000], [T, T], 32, 4, 128, 16, seed=107)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    sm = float(sm_of(bt))
+    out = torch.empty_like(db.q)
+    seq_lens = db.seq_lens.clone()
+    q = db.q.clone()
+
+    def step():
+        K.paged_attn_e4m3_verify(q, db.cu_q, T, db.k_cache, db.v_cache, db.block_table, seq_lens, float(sc[0]),
+                                 float(sc[1]), sm, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(108)
+    for rep, lens in enumerate(([2000, 40], [41, 1999], [1000, 1000], [555, 64])):
+        lens = np.asarray(lens, np.int32)
+        qn = rng.standard_normal(bt.q.shape).astype(np.float16)
+        seq_lens.copy_(torch.from_numpy(lens))
+        q.copy_(torch.from_numpy(qn))
+        out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(replayed, out), f"replay {rep} differs from the eager call"
+        ref, _ = paged_attention(qn, kc, vc, bt.block_table, lens, bt.cu_q_lens, sc[0], sc[1], sm)
+        assert_close_attn(replayed.cpu().numpy(), ref, f"replay {rep}")
