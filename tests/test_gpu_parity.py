@@ -823,3 +823,27 @@ def test_graph_replay_chunk_follows_lengths(K):
         assert torch.equal(replayed, out), f"replay {rep} differs from the eager call"
         ref, _ = paged_attention(qn, kc, vc, bt.block_table, lens, bt.cu_q_lens, sc[0], sc[1], sm)
         assert_close_attn(replayed.cpu().numpy(), ref, f"replay {rep}")
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_decode_sequences_without_keys(K, S):
+    """Decode rows whose sequence has no keys (as on a context shard that holds
+    none of a sequence's pages) produce zeros, directly and through the split
+    partials, and leave the other rows unaffected."""
+    bt = make_batch([300, 5, 700, 64], [1] * 4, 32, 4, 128, 16, seed=109)
+    _, sc = oracle_scales(bt)
+    db = DeviceBatch(bt)
+    _gpu_write(K, db, sc[0], sc[1])
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    sm = float(sm_of(bt))
+    lens = bt.seq_lens.copy()
+    lens[[1, 3]] = 0
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert not ref[[1, 3]].any()
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S) if S > 1 else None
+    if ws is not None:
+        K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
+    out = K.paged_attn_e4m3_decode(db.q, db.k_cache, db.v_cache, db.block_table, dev(lens), float(sc[0]),
+                                   float(sc[1]), sm, num_splits=S, workspace=ws).cpu().numpy()
+    assert not out[[1, 3]].astype(np.float64).any()
+    assert_close_attn(out, ref, f"S={S}")
