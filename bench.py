@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # FETCH_SIZE / WRITE_SIZE runs (`bench.py --counter-pass`), scaled by the same
 # counters' reading of a 1 GiB device copy. Valid only for the kernel source
 # they were taken on (sha256 prefix); otherwise the traffic is reported as null.
-MEASURED_TRAFFIC = {"source_sha256_prefix": "1abe69f23a34c9fc", "read_bytes": 137017155,
+MEASURED_TRAFFIC = {"source_sha256_prefix": "0096e1d45a991727", "read_bytes": 136806912,
                     "write_bytes": 1081344}
 
 
@@ -714,7 +714,7 @@ def main():
                                    if p in ("4k", "32k", "256k")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "attn_split_kernel<128,16,1,8>", "kernel_us": main["attn_kernel_us"]},
+                     "kernel": "attn_split_kernel<128,16,1,8,false>", "kernel_us": main["attn_kernel_us"]},
         "cpu_baseline": cpu,
         "points": results,
     }

@@ -78,6 +78,29 @@ __device__ __forceinline__ void load_pages(PageRegs<P>& pr, const int32_t* __res
   for (int pc = 0; pc < PageRegs<P>::NV; ++pc) pr.v[pc] = btrow[min((t0 + 16 * g + pc * P) / P, last)];
 }
 
+// Page ids of one 64-key tile (pages of >= 16 keys) taken from a block-table
+// row held across the wavefront: lane l holds row entries l, l + 64, l + 128
+// and l + 192 (rows of at most 256 pages). Same indices as load_pages, no
+// memory access.
+__device__ __forceinline__ int32_t row_entry(const int32_t (&rowv)[4], int idx) {
+  const int addr = (idx & 63) << 2;
+  const int32_t v0 = __builtin_amdgcn_ds_bpermute(addr, rowv[0]);
+  const int32_t v1 = __builtin_amdgcn_ds_bpermute(addr, rowv[1]);
+  const int32_t v2 = __builtin_amdgcn_ds_bpermute(addr, rowv[2]);
+  const int32_t v3 = __builtin_amdgcn_ds_bpermute(addr, rowv[3]);
+  const int k = idx >> 6;
+  return k == 0 ? v0 : (k == 1 ? v1 : (k == 2 ? v2 : v3));
+}
+
+template <int P>
+__device__ __forceinline__ void pages_from_row(PageRegs<P>& pr, const int32_t (&rowv)[4], int t0, int last, int n,
+                                               int g) {
+  static_assert(P >= 16, "one page id per lane for K and for V");
+  const int krel = 16 * (n >> 2) + (n & 3);
+  pr.k[0] = row_entry(rowv, min((t0 + krel) / P, last));
+  pr.v[0] = row_entry(rowv, min((t0 + 16 * g) / P, last));
+}
+
 // K/V bytes are read exactly once per call, so they are loaded non-temporally
 // (streamed past the caches instead of evicting the block table, Q and the
 // partials). The loads are unconditional: a tile never extends past the split
@@ -326,7 +349,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
   }
 }
 
-template <int D, int P, int NB, int W>
+template <int D, int P, int NB, int W, bool SHORT = false>
 __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a) {
   constexpr int NC = D / 32;
   constexpr int NBLK = D / 16;
@@ -342,6 +365,21 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int n = lane & 15;
   const int g = lane >> 4;
   const int S = a.num_splits;
+  // SHORT (decode over pages of >= 16 keys, one round of 8-wavefront
+  // workgroups, at most one tile per wavefront): the start-up is the whole
+  // kernel, so it is cut short. The block-table row of sequence blockIdx.z
+  // (the plan's sequence whenever the plan is the plain grid, e.g. equal
+  // lengths) loads beside the work plan's context lengths; when the plan
+  // confirms it and the row has at most 256 pages, the first tiles' page ids
+  // come from it, one round trip earlier. Indices stay inside the row.
+  constexpr bool kRowPrefetch = SHORT;
+  static_assert(!SHORT || (NB == 1 && P >= 16 && W == 8), "short start-up: decode, pages of >= 16 keys, 8 waves");
+  int32_t rowv[4] = {0, 0, 0, 0};
+  if constexpr (kRowPrefetch) {
+    const int32_t* grow = a.block_table + (int64_t)blockIdx.z * a.max_pages;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rowv[k] = grow[min(lane + 64 * k, a.max_pages - 1)];
+  }
   const SplitItem itm = plan_item(a.seq_lens, a.batch, a.n_kv_heads, S,
                                   blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), lane);
   if (!itm.valid) return;  // past the last item (uniform over the workgroup)
@@ -360,6 +398,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   T = min(T, a.max_q_len);
   const int G = a.group;
   const int nrows = T * G;
+  // no query rows (a verify sequence without tokens): nothing to write; the
+  // short start-up relies on it (it clamps row indices to nrows - 1)
+  if (SHORT && nrows <= 0) return;
   const int start = s * itm.chunk;
   const int end = min(start + itm.chunk, L);
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
@@ -424,15 +465,43 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   // wavefront 0 stores it: with the loads in a wave-uniform branch the
   // compiler could no longer count them exactly, and its wait before reusing
   // their registers would also wait for the tile in flight.
+  // (The short start-up differs: see kRowPrefetch and kOwnQ.)
+  // Page ids of the wavefront's first two tiles. The short start-up takes
+  // them before Q is loaded: the fallback's loads then precede Q's, and the
+  // first tile waits for no Q load.
+  int it = wave;
+  PageRegs<P> pa, pb;
+  TileRegs<D, P> ra;
+  auto first_pages = [&]() {
+    // Page ids are loaded unconditionally (they are clamped to the sequence's
+    // last page, and every block-table row has an entry): a load on only one
+    // side of a branch would make the compiler's wait counts inexact.
+    if constexpr (kRowPrefetch) {
+      if (a.max_pages <= 256 && b == (int)blockIdx.z) {
+        pages_from_row<P>(pa, rowv, start + it * kTile, last, n, g);
+        pages_from_row<P>(pb, rowv, start + (it + W) * kTile, last, n, g);
+      } else {
+        load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+        load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+      }
+    } else {
+      load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
+      load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
+    }
+  };
+  if constexpr (kRowPrefetch) first_pages();
   // Q operand: dims g*D/4 + 8c + i of row n of each 16-row block.
   f16x8 qraw[NB][NC];
   int lim[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int rr = nb * 16 + n;
+    // the short start-up loads a real row for the padding rows too (masked,
+    // never written): no lane skips the loads, so no path through the
+    // start-up has a different number of loads in flight
+    const int rr = kRowPrefetch ? min(n, nrows - 1) : nb * 16 + n;
     const int i = rr / G;
-    lim[nb] = rr < nrows ? min(end, L - T + i + 1) : 0;
-    if (rr < nrows) {
+    lim[nb] = nb * 16 + n < nrows ? min(end, L - T + i + 1) : 0;
+    if (kRowPrefetch || rr < nrows) {
       const int h = kvh * G + rr % G;
       const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + h) * D + 16 * g;
 #pragma unroll
@@ -443,15 +512,12 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
       for (int c = 0; c < NC; ++c) qraw[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  int it = wave;
-  PageRegs<P> pa, pb;
-  TileRegs<D, P> ra;
-  // Page ids are loaded unconditionally (they are clamped to the sequence's
-  // last page, and every block-table row has an entry): a load on only one
-  // side of a branch would make the compiler's wait counts inexact.
-  load_pages<P>(pa, btrow, start + it * kTile, last, n, g);
-  load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-  if (wave == 0) {
+  if constexpr (!kRowPrefetch) first_pages();
+  // Short start-up: the first tile is issued before Q is stored, and every
+  // wavefront stores its own copy of Q (the same bytes in the same place) and
+  // reads only after its own store, so no barrier.
+  constexpr bool kOwnQ = kRowPrefetch;
+  if (!kOwnQ && wave == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -464,8 +530,15 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   // the verify pipeline stages every tile, the first included, through LDS
   constexpr bool kStaged = NB == 2 && P >= 16;
   __asm__ volatile("" ::: "memory");
-  if (!kStaged && it < ntiles) load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (!kStaged && it < ntiles) {
+    load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
+    // a wavefront without tiles never reads Q
+    if constexpr (kOwnQ) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sm_q[0][c][lane] = qraw[0][c];
+    }
+  }
+  if constexpr (!kOwnQ) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   float m_ref[NB], m_max[NB], l_run[NB];
   f32x4 o[NB][NBLK];
@@ -629,6 +702,14 @@ hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
   // workgroups per CU, which halves the number of rounds.
   if constexpr (NB == 1) {
     if ((int64_t)a.num_splits * a.n_kv_heads * a.batch <= device_cus()) {
+      // at most one 64-key tile per wavefront (splits are multiples of 64
+      // keys): the short start-up
+      if constexpr (P >= 16) {
+        if (a.max_pages <= 256 && (int64_t)a.max_pages * P <= (int64_t)64 * 8 * a.num_splits) {
+          attn_split_kernel<D, P, 1, 8, true><<<grid, dim3(64 * 8), 0, stream>>>(a);
+          return hipGetLastError();
+        }
+      }
       attn_split_kernel<D, P, 1, 8><<<grid, dim3(64 * 8), 0, stream>>>(a);
       return hipGetLastError();
     }
