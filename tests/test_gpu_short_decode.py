@@ -6,8 +6,9 @@ each wavefront storing its own copy of Q, no start-up barrier). Compared with
 the fp64 oracle with equal lengths (the plan is the plain grid, so the
 prefetched row is the one used), ragged lengths (the plan packs items
 differently, so the page ids are loaded after the plan), a sequence without
-keys, a group smaller than the 16-row block (padding rows), and an MTP verify
-small enough for one 16-row block, with a sequence that has no query tokens."""
+keys, a group smaller than the 16-row block (padding rows), an MTP verify
+small enough for one 16-row block, with a sequence that has no query tokens,
+and the fused step that appends the new token in the same launch."""
 import numpy as np
 import pytest
 import torch
@@ -100,3 +101,29 @@ def test_small_verify_one_block(K):
     assert short_launch(bt, S, max_q=2)
     out, ref = run(K, bt, S, verify=True)
     assert_close_attn(out, ref, "small verify")
+
+
+def test_append_with_prefetched_row(K):
+    """The fused step (the new token quantised into its slot in the same launch)
+    on the tensor-parallel share: cache bytes bit-exact against the oracle and
+    the output against the oracle over the whole context."""
+    bt = make_batch([4096] * 32, [1] * 32, 8, 1, 128, 16, seed=9850)
+    S = 8
+    assert short_launch(bt, S)
+    _, sc = oracle_scales(bt)
+    ks, vs = float(sc[0]), float(sc[1])
+    sm = float(np.float32(1.0 / np.sqrt(bt.head_dim)))
+    db = DeviceBatch(bt)
+    prior, new = dev(bt.prior_rows()), dev(bt.new_token_rows())
+    K.kv_quant_write(db.k[prior].contiguous(), db.v[prior].contiguous(), db.slots[prior].contiguous(), ks, vs,
+                     db.k_cache, db.v_cache)
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
+    K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
+    out = K.paged_attn_e4m3_decode_append(db.q, db.k[new].contiguous(), db.v[new].contiguous(), db.k_cache,
+                                          db.v_cache, db.block_table, db.seq_lens, ks, vs, sm, num_splits=S,
+                                          workspace=ws).cpu().numpy()
+    kc, vc = oracle_caches(bt, sc[0], sc[1])
+    assert np.array_equal(db.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy(), vc)
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, "append, prefetched row")
