@@ -366,7 +366,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int g = lane >> 4;
   const int S = a.num_splits;
   // SHORT (decode over pages of >= 16 keys, one round of 8-wavefront
-  // workgroups, at most one tile per wavefront): the start-up is the whole
+  // workgroups, at most one tile per wavefront): the start-up is most of the
   // kernel, so it is cut short. The block-table row of sequence blockIdx.z
   // (the plan's sequence whenever the plan is the plain grid, e.g. equal
   // lengths) loads beside the work plan's context lengths; when the plan
