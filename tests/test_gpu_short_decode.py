@@ -67,13 +67,23 @@ def test_equal_lengths_prefetched_row(K, P, S):
     assert_close_attn(out, ref, f"equal lengths P={P} S={S}")
 
 
-@pytest.mark.parametrize("seed", range(3))
-def test_ragged_lengths_plan_packs_items(K, seed):
+def test_equal_lengths_head_dim_64(K):
+    """head_dim 64, 8 query heads per kv-head, 2 kv-heads: 16 sequences of
+    2,048 keys at 4 splits (one tile per wavefront)."""
+    bt = make_batch([2048] * 16, [1] * 16, 16, 2, 64, 16, seed=9805)
+    S = 4
+    assert short_launch(bt, S)
+    out, ref = run(K, bt, S)
+    assert_close_attn(out, ref, "equal lengths head_dim 64")
+
+
+@pytest.mark.parametrize("seed,P", [(0, 16), (1, 16), (2, 16), (3, 32), (4, 64)])
+def test_ragged_lengths_plan_packs_items(K, seed, P):
     rng = np.random.default_rng(9810 + seed)
     B = 24
     lens = [int(x) for x in rng.integers(1, 2049, B)]
     lens[0] = 2048  # the longest row sets the split size
-    bt = make_batch(lens, [1] * B, 16, 2, 128, 16, seed=9820 + seed)
+    bt = make_batch(lens, [1] * B, 16, 2, 128, P, seed=9820 + seed)
     S = 4
     assert short_launch(bt, S)
     out, ref = run(K, bt, S)
