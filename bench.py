@@ -300,16 +300,20 @@ class Point:
             o = torch.empty_like(q)
             n = len(self.sets)
 
-            def call(i, q=q, cu=cu, btab=btab, sl=sl, S=S, ws=ws, o=o, mq=int(ql.max())):
+            def call(i, q=q, cu=cu, btab=btab, sl=sl, S=S, ws=ws, o=o, mq=int(ql.max()), full=False):
                 kc, vc = self.sets[i % n]
                 kw = dict(num_splits=S, workspace=ws)
-                kw.update(partials_only=True) if S > 1 else kw.update(out=o)
+                kw.update(partials_only=True) if (S > 1 and not full) else kw.update(out=o)
                 K.paged_attn_e4m3_verify(q, cu, mq, kc, vc, btab, sl, self.ks, self.vs, self.sm, **kw)
 
-            sec = self._time_graph(call, max(launches // n, 1) * n)
+            nl = max(launches // n, 1) * n
+            sec = self._time_graph(call, nl)
+            step = self._time_graph(lambda i, c=call: c(i, full=True), nl)
             kv = int(L) * len(idx) * self.Hkv * self.D * 2
             out[str(L)] = {"sequences": int(len(idx)), "query_rows": int(len(rows)), "num_splits": int(S),
-                           "kernel_us": sec * 1e6, "kv_gbs": kv / sec / 1e9}
+                           "kernel_us": sec * 1e6, "kv_gbs": kv / sec / 1e9,
+                           "step_us": step * 1e6, "query_tokens_per_s_per_layer": len(rows) / step,
+                           "step": "verify + reduce over this bucket's sequences alone"}
         return out
 
     def time_fill(self, k_src, v_src, launches=12, replays=3):
@@ -479,6 +483,41 @@ def cpu_baseline(seconds_target=10.0):
     }
 
 
+def streaming_read_ceiling(K, torch, elems_per_tensor=1 << 30, reps=5):
+    """HBM streaming-read rate of committed code: the library's calibration
+    scan (kv_calibrate_amax: contiguous fp16, 16-byte non-temporal loads, a
+    packed max per element) over two tensors of 2 GiB each. The call is
+    synchronous (it reads its status back), so HIP events bracket its kernels,
+    the few-byte readback and the host's return; the same call on a 64 Ki-element
+    input measures that fixed part, which is subtracted. Fastest of `reps`."""
+    big = torch.ones((2, elems_per_tensor), dtype=torch.float16, device="cuda")
+    small = torch.ones((2, 1 << 16), dtype=torch.float16, device="cuda")
+    amax = torch.empty(2, dtype=torch.float32, device="cuda")
+    scale = torch.empty(2, dtype=torch.float32, device="cuda")
+
+    def best(x):
+        t = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            K.kv_calibrate_amax(x, amax, scale)
+            e1.record()
+            torch.cuda.synchronize()
+            t = min(t, e0.elapsed_time(e1) / 1e3)
+        return t
+
+    best(big)  # warm-up
+    t_big, t_small = best(big), best(small)
+    nbytes = big.numel() * 2
+    del big
+    torch.cuda.empty_cache()
+    return {"gbs": nbytes / (t_big - t_small) / 1e9, "bytes": nbytes, "call_us": t_big * 1e6,
+            "fixed_us": t_small * 1e6,
+            "method": "kv_calibrate_amax over 2 x 2 GiB fp16 (HIP events, minus the same call on 2 x 64 Ki "
+                      "elements), fastest of %d" % reps}
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -493,6 +532,16 @@ def counter_pass(K, torch, make_config, point="4k"):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    if point == "chunk":
+        # the mixed workload's 2,048-token chunk over 30,000 prior keys (layer 0's scales)
+        from synth.workloads import make_mixed_calibration
+        _, scale, _ = K.kv_calibrate_amax(torch.from_numpy(make_mixed_calibration()[:2]).cuda())
+        ml = MixedLayer(K, torch, (float(scale[0].item()), float(scale[1].item())))
+        for i in range(12):
+            ml.chunk(i)
+        torch.cuda.synchronize()
+        log(f"counter pass: copy {COPY_BYTES} B x3, 12 chunk attention launches ({ml.chunk_flops} flops each)")
+        return
     bt = make_config(2 if point == "4k" else 3)
     k_src = torch.from_numpy(bt.k).cuda()
     v_src = torch.from_numpy(bt.v).cuda()
@@ -502,7 +551,7 @@ def counter_pass(K, torch, make_config, point="4k"):
     else:
         S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
                              n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
-        nsets = 2
+        nsets = 3
     pt = Point(K, torch, point, bt, k_src, v_src, calib, S, nsets)
     for i in range(12):
         pt.attend(i)
@@ -523,7 +572,7 @@ def main():
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager launches for hardware-counter runs: a 1 GiB device copy "
                          "(reference for the byte counters), then 4k decode attention launches")
-    ap.add_argument("--counter-point", default="4k", choices=("4k", "mtp3"),
+    ap.add_argument("--counter-point", default="4k", choices=("4k", "mtp3", "chunk"),
                     help="workload of the counter pass's attention launches")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -594,7 +643,7 @@ def main():
             S = (K.default_splits(bt.batch, bt.n_kv_heads, 4096) if p == "4k_f16" else
                  K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
                                  n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max())))
-            nsets, steps = (6, args.steps) if p == "4k_f16" else (2, max(10, args.steps // 3))
+            nsets, steps = (6, args.steps) if p == "4k_f16" else (3, max(10, args.steps // 3))
         elif p == "mtp3":
             bt = make_config(3)
             k_src = torch.from_numpy(bt.k).cuda()
@@ -602,7 +651,7 @@ def main():
             calib = torch.from_numpy(np.stack([bt.calib_k.reshape(-1), bt.calib_v.reshape(-1)])).cuda()
             S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
                                  n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
-            nsets, steps = 2, max(10, args.steps // 3)
+            nsets, steps = 3, max(10, args.steps // 3)  # 3 x 189 MB of KV: no set stays in the 256 MB MALL
         elif p == "mixed":
             from synth.workloads import make_mixed_calibration
             calib = torch.from_numpy(make_mixed_calibration()).cuda()
@@ -664,6 +713,8 @@ def main():
                      "attention with the new tokens appended"),
             "kv_cache": "fp16" if pt.f16 else "e4m3",
             "attn_kernel_us": kern * 1e6, "attn_kernel_gbs": pt.alg_bytes / kern / 1e9,
+            "attn_kernel": K.kvfp8_attn_kernel_name(pt.B, pt.Hq, pt.Hkv, pt.D, pt.P, bt.max_pages, pt.max_q, S,
+                                                    pt.f16),
             "graph_replay_matches_eager": same, "cache_sets": nsets,
         }
         if fill is not None:
@@ -692,6 +743,16 @@ def main():
         log("timing the oracle on the host")
         cpu = cpu_baseline()
     achieved = main["attn_kernel_gbs"]
+    log("measuring the streaming-read ceiling")
+    ceiling = streaming_read_ceiling(K, torch)
+    log(f"streaming-read ceiling: {json.dumps(ceiling)}")
+    tps = {}
+    for p, key in (("4k", "4k"), ("32k", "32k_derived_decode_b32"), ("256k", "256k")):
+        if p in results:
+            tps[key] = results[p]["tokens_per_s_per_layer"]
+    bucket = results.get("mtp3", {}).get("buckets", {}).get("32768")
+    if bucket is not None:
+        tps["32k_mtp3_bucket_query_tokens"] = bucket["query_tokens_per_s_per_layer"]
     line = {
         "metric": METRIC,
         "value": main["kv_gbs"],
@@ -710,11 +771,17 @@ def main():
                    "page_size": main["page_size"], "num_splits": main["num_splits"],
                    "kv_cache": "e4m3 (OCP), per-layer K/V scales", "accumulate": "f32"},
         "pct_hbm_peak": 100.0 * main["kv_gbs"] / HBM_PEAK_GBS,
-        "tokens_per_s_per_layer": {p: r["tokens_per_s_per_layer"] for p, r in results.items()
-                                   if p in ("4k", "32k", "256k")},
+        "tokens_per_s_per_layer": tps,
+        "tokens_per_s_note": ("4k and 256k: the decode workloads; 32k_derived_decode_b32: the 4k decode shape at "
+                              "32,768 keys (derived, not one of the five workloads); "
+                              "32k_mtp3_bucket_query_tokens: the MTP3 workload's 32,768-key sequences alone "
+                              "(query tokens through verify + reduce)"),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "attn_split_kernel<128,16,1,8,false>", "kernel_us": main["attn_kernel_us"]},
+                     "kernel": main["attn_kernel"], "kernel_us": main["attn_kernel_us"],
+                     "measured_streaming_read_gbs": ceiling["gbs"],
+                     "frac_of_measured_streaming_read": achieved / ceiling["gbs"],
+                     "streaming_read": ceiling},
         "cpu_baseline": cpu,
         "points": results,
     }

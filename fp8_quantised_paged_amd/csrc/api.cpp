@@ -207,6 +207,36 @@ KVFP8_API size_t kvfp8_attn_workspace_bytes(int64_t n_rows, int32_t n_q_heads, i
          sizeof(float);
 }
 
+KVFP8_API const char* kvfp8_attn_kernel_name(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq,
+                                             int32_t max_q_len, int32_t num_splits, int32_t f16_kv) {
+  thread_local char name[96];
+  name[0] = '\0';
+  if (batch <= 0 || batch > 65535 || n_q_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > 65535 ||
+      n_q_heads % n_kv_heads != 0 || (head_dim != 64 && head_dim != 128) || !supported_page(page_size) ||
+      max_pages_per_seq <= 0 || max_q_len < 1 || num_splits < 1 || num_splits > kMaxSplits)
+    return name;
+  kvfp8::AttnArgs a{};
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = n_q_heads / n_kv_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.num_splits = num_splits;
+  a.max_q_len = max_q_len;
+  const int64_t rows = (int64_t)max_q_len * a.group;
+  if (f16_kv) {
+    if (rows <= kSplitRows) kvfp8::attn_split_f16_kernel_name(a, (int)rows, name, sizeof(name));
+  } else if (rows <= kSplitRows) {
+    kvfp8::attn_split_kernel_name(a, (int)rows, name, sizeof(name));
+  } else if (num_splits == 1) {
+    kvfp8::attn_chunk_kernel_name(a, name, sizeof(name));
+  }
+  return name;
+}
+
 KVFP8_API int32_t kv_calibrate_amax(const uint16_t* x_f16, int64_t n_tensors, int64_t n_elems,
                                     float* amax_out, float* scale_out, hipStream_t stream) {
   if (n_tensors < 0 || n_elems < 0) return fail(KVFP8_INVALID_ARG, "negative size");

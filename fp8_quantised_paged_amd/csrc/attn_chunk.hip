@@ -15,6 +15,8 @@
 // when the (query tile, kv-head) plane divides evenly, the linear index is
 // remapped so that each XCD serves a contiguous run of query tiles of as few
 // kv-heads as possible, and its L2 holds one head's K/V stream.
+#include <cstdio>
+
 #include "kvfp8_internal.h"
 
 #include <type_traits>
@@ -492,6 +494,10 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+void attn_chunk_kernel_name(const AttnArgs& a, char* buf, size_t n) {
+  snprintf(buf, n, "attn_chunk_kernel<%d,%d>", a.head_dim, a.page_size);
+}
 
 hipError_t launch_attn_chunk(const AttnArgs& a, hipStream_t stream) {
   if (a.out == nullptr || a.cu_q_lens == nullptr) return hipErrorInvalidValue;

@@ -26,6 +26,8 @@
 //    dimension-major V page.
 // Scores are scaled once per tile by k_scale * sm_scale * log2(e) (folded into
 // the exp2 argument); v_scale is applied once to the merged accumulator.
+#include <cstdio>
+
 #include "kvfp8_internal.h"
 #include "split_plan.h"
 
@@ -691,21 +693,37 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   }
 }
 
+// The launch shape for a call. One 16-row block (decode) whose whole grid fits
+// in one round of the compute units runs 8 wavefronts per workgroup, one
+// workgroup per CU, so a CU's wavefronts are of one age and finish together
+// (two 4-wavefront workgroups on one CU finish apart under the hardware's
+// oldest-first issue). Larger grids, and two blocks (verify, LDS-bound), run 4
+// wavefronts, two workgroups per CU, which halves the number of rounds. An
+// 8-wavefront decode launch over pages of >= 16 keys whose splits hold at most
+// one 64-key tile per wavefront takes the short start-up.
+struct SplitLaunch {
+  int nb;
+  int w;
+  bool short_start;
+};
+
+SplitLaunch choose_split_launch(const AttnArgs& a, int rows) {
+  SplitLaunch c{rows <= 16 ? 1 : 2, 4, false};
+  if (c.nb == 1 && (int64_t)a.num_splits * a.n_kv_heads * a.batch <= device_cus()) {
+    c.w = 8;
+    c.short_start = a.page_size >= 16 && a.max_pages <= 256 &&
+                    (int64_t)a.max_pages * a.page_size <= (int64_t)kTile * 8 * a.num_splits;
+  }
+  return c;
+}
+
 template <int D, int P, int NB>
-hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch3(const AttnArgs& a, const SplitLaunch& c, hipStream_t stream) {
   dim3 grid((unsigned)a.num_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);
-  // One 16-row block (decode) whose whole grid fits in one round of the
-  // compute units: 8 wavefronts per workgroup, one workgroup per CU, so a CU's
-  // wavefronts are of one age and finish together (two 4-wavefront workgroups
-  // on one CU finish apart under the hardware's oldest-first issue). Larger
-  // grids, and two blocks (verify, LDS-bound), run 4 wavefronts, two
-  // workgroups per CU, which halves the number of rounds.
   if constexpr (NB == 1) {
-    if ((int64_t)a.num_splits * a.n_kv_heads * a.batch <= device_cus()) {
-      // at most one 64-key tile per wavefront (splits are multiples of 64
-      // keys): the short start-up
+    if (c.w == 8) {
       if constexpr (P >= 16) {
-        if (a.max_pages <= 256 && (int64_t)a.max_pages * P <= (int64_t)64 * 8 * a.num_splits) {
+        if (c.short_start) {
           attn_split_kernel<D, P, 1, 8, true><<<grid, dim3(64 * 8), 0, stream>>>(a);
           return hipGetLastError();
         }
@@ -720,8 +738,9 @@ hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
 
 template <int D, int P>
 hipError_t launch2(const AttnArgs& a, int rows, hipStream_t stream) {
-  if (rows <= 16) return launch3<D, P, 1>(a, stream);
-  return launch3<D, P, 2>(a, stream);
+  const SplitLaunch c = choose_split_launch(a, rows);
+  if (c.nb == 1) return launch3<D, P, 1>(a, c, stream);
+  return launch3<D, P, 2>(a, c, stream);
 }
 
 template <int D>
@@ -737,6 +756,12 @@ hipError_t launch1(const AttnArgs& a, int rows, hipStream_t stream) {
 }
 
 }  // namespace
+
+void attn_split_kernel_name(const AttnArgs& a, int rows_per_kvh, char* buf, size_t n) {
+  const SplitLaunch c = choose_split_launch(a, rows_per_kvh);
+  snprintf(buf, n, "attn_split_kernel<%d,%d,%d,%d,%s>", a.head_dim, a.page_size, c.nb, c.w,
+           c.short_start ? "true" : "false");
+}
 
 hipError_t launch_attn_split(const AttnArgs& a, int rows_per_kvh, hipStream_t stream) {
   if (a.head_dim == 128) return launch1<128>(a, rows_per_kvh, stream);

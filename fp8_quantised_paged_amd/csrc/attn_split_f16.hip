@@ -14,6 +14,8 @@
 // order: the B operand of the PV product as it stands. Dimensions follow the
 // E4M3 kernel's order (lane group g holds dims g*D/4 .. g*D/4 + D/4 - 1 of its
 // key row, and the Q operand matches).
+#include <cstdio>
+
 #include "kvfp8_internal.h"
 #include "split_plan.h"
 
@@ -425,6 +427,12 @@ hipError_t launch1_f16(const AttnArgs& a, int rows, hipStream_t stream) {
 }
 
 }  // namespace
+
+void attn_split_f16_kernel_name(const AttnArgs& a, int rows_per_kvh, char* buf, size_t n) {
+  const int nb = rows_per_kvh <= 16 ? 1 : 2;
+  const int w = (nb == 1 && (int64_t)a.num_splits * a.n_kv_heads * a.batch <= device_cus()) ? 8 : 4;
+  snprintf(buf, n, "attn_split_f16_kernel<%d,%d,%d,%d>", a.head_dim, a.page_size, nb, w);
+}
 
 hipError_t launch_attn_split_f16(const AttnArgs& a, int rows_per_kvh, hipStream_t stream) {
   if (rows_per_kvh < 1 || rows_per_kvh > 32) return hipErrorNotSupported;

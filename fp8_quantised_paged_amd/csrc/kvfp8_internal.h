@@ -114,6 +114,11 @@ hipError_t launch_attn_split(const AttnArgs& a, int rows_per_kvh, hipStream_t st
 hipError_t launch_attn_split_f16(const AttnArgs& a, int rows_per_kvh, hipStream_t stream);
 // Query-tiled causal chunk kernel (long q_len).
 hipError_t launch_attn_chunk(const AttnArgs& a, hipStream_t stream);
+// Name of the kernel instantiation each attention launcher chooses for these
+// arguments (rows_per_kvh: query rows per kv-head), written to buf.
+void attn_split_kernel_name(const AttnArgs& a, int rows_per_kvh, char* buf, size_t n);
+void attn_split_f16_kernel_name(const AttnArgs& a, int rows_per_kvh, char* buf, size_t n);
+void attn_chunk_kernel_name(const AttnArgs& a, char* buf, size_t n);
 hipError_t launch_split_reduce(const float* ws_o, const float* ws_m, const float* ws_l,
                                int32_t n_rows, int32_t n_q_heads, int32_t head_dim,
                                int32_t num_splits, uint16_t* out, float* lse,

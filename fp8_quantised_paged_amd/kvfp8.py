@@ -31,6 +31,7 @@ EXPORTED = (
     "paged_attn_f16_verify",
     "split_reduce_fp32",
     "kvfp8_attn_workspace_bytes",
+    "kvfp8_attn_kernel_name",
     "kvfp8_status_str",
     "kvfp8_last_error",
     "kvfp8_e4m3_encode_f32",
@@ -57,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "kvfp8_status_str": (ctypes.c_char_p, [I32]),
         "kvfp8_last_error": (ctypes.c_char_p, []),
         "kvfp8_attn_workspace_bytes": (SZ, [I64, I32, I32, I32]),
+        "kvfp8_attn_kernel_name": (ctypes.c_char_p, [I32, I32, I32, I32, I32, I32, I32, I32, I32]),
         "kv_calibrate_amax": (I32, [P, I64, I64, P, P, P]),
         "kv_quant_write": (I32, [P, P, P, I64, I32, I32, I32, I64, F32, F32, P, P, P]),
         "paged_attn_e4m3_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, F32, F32,
@@ -131,9 +133,30 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = 
         raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
 
 
+def _check_rows(name: str, out: Optional[torch.Tensor], q: torch.Tensor, block_table: torch.Tensor,
+                seq_lens: torch.Tensor, batch: int, workspace: Optional[torch.Tensor]):
+    """Shape checks the C ABI cannot make (it sees pointers, not buffer sizes):
+    out has q's shape, the block table and the context lengths have one row per
+    sequence, and a workspace is a contiguous fp32 GPU tensor."""
+    if out is not None and tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"{name}: out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    if block_table.shape[0] != batch:
+        raise ValueError(f"{name}: block_table must have {batch} rows (one per sequence), got {block_table.shape[0]}")
+    if seq_lens.shape[0] != batch:
+        raise ValueError(f"{name}: seq_lens must have {batch} entries (one per sequence), got {seq_lens.shape[0]}")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.float32)
+
+
 def kvfp8_attn_workspace_bytes(n_rows: int, n_q_heads: int, head_dim: int, num_splits: int) -> int:
     return int(_lib.kvfp8_attn_workspace_bytes(n_rows, n_q_heads, head_dim, num_splits))
 
+
+def kvfp8_attn_kernel_name(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, page_size: int,
+                           max_pages_per_seq: int, max_q_len: int, num_splits: int, f16_kv: bool = False) -> str:
+    """Kernel instantiation an attention call with these arguments launches ("" if none)."""
+    return _lib.kvfp8_attn_kernel_name(batch, n_q_heads, n_kv_heads, head_dim, page_size, max_pages_per_seq,
+                                       max_q_len, num_splits, int(bool(f16_kv))).decode()
 
 def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Optional[int] = None,
                    cus: int = 256, seq_lens=None, n_q_heads: Optional[int] = None, q_len: int = 1) -> int:
@@ -263,6 +286,7 @@ def paged_attn_e4m3_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_e4m3_decode", out, q, block_table, seq_lens, B, workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.paged_attn_e4m3_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -297,6 +321,7 @@ def paged_attn_e4m3_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_e4m3_decode_append", out, q, block_table, seq_lens, B, workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.paged_attn_e4m3_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
@@ -330,6 +355,7 @@ def paged_attn_e4m3_verify(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: 
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_e4m3_verify", out, q, block_table, seq_lens, B, workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.paged_attn_e4m3_verify(q.data_ptr(), cu_q_lens.data_ptr(), total_q, int(max_q_len),
@@ -368,6 +394,7 @@ def paged_attn_e4m3_verify_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_e4m3_verify_append", out, q, block_table, seq_lens, B, workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.paged_attn_e4m3_verify_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cu_q_lens.data_ptr(),
@@ -408,6 +435,7 @@ def paged_attn_f16_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_f16_decode", out, q, block_table, seq_lens, B, workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.paged_attn_f16_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -439,6 +467,7 @@ def paged_attn_f16_verify(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: i
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_f16_verify", out, q, block_table, seq_lens, B, workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.paged_attn_f16_verify(q.data_ptr(), cu_q_lens.data_ptr(), total_q, int(max_q_len),

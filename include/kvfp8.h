@@ -87,6 +87,18 @@ const char* kvfp8_last_error(void);
 size_t kvfp8_attn_workspace_bytes(int64_t n_rows, int32_t n_q_heads, int32_t head_dim,
                                   int32_t num_splits);
 
+/* Name of the kernel instantiation an attention call with these arguments
+ * launches on the current device, e.g. "attn_split_kernel<128,16,1,8,false>"
+ * (template arguments: head_dim, page_size, 16-row query blocks, wavefronts
+ * per workgroup, short start-up), "attn_split_f16_kernel<...>" (f16_kv != 0:
+ * the FP16-cache twins) or "attn_chunk_kernel<head_dim,page_size>". Decode
+ * calls pass max_q_len = 1. Returns "" for arguments no call accepts. A static
+ * thread-local string, valid until the next call on that thread; launches
+ * nothing. For tests and benchmarks that must name the kernel they exercise. */
+const char* kvfp8_attn_kernel_name(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                   int32_t page_size, int32_t max_pages_per_seq, int32_t max_q_len,
+                                   int32_t num_splits, int32_t f16_kv);
+
 /* Per-tensor calibration ([P2] Changes: offline calibration of the per-layer
  * K/V scales; [P2] Validation boundary: no unit-scale fallback). For each of
  * n_tensors contiguous fp16 rows of n_elems elements:

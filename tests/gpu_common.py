@@ -17,12 +17,22 @@ def dev(a, dtype=None):
     return t.cuda()
 
 
-def assert_close_attn(gpu_f16: np.ndarray, ref: np.ndarray, what: str = ""):
+def assert_close_attn(gpu_f16: np.ndarray, ref: np.ndarray, what: str = "", strict: bool = False):
     """|gpu - ref| <= 2e-3 + 1e-2 * |ref| elementwise (fp16 output, fp32
-    accumulation, against the fp64 oracle)."""
+    accumulation, against the fp64 oracle). With strict, the largest absolute
+    error must also be at most 2e-3 outright: the literal bound, which an fp16
+    output can meet wherever |ref| stays below 8 (half an fp16 ulp there is at
+    most 2^-9), as in every N(0, 1) workload; the workload with Student-t outlier
+    channels, where |ref| reaches tens, keeps the combined rule alone. Prints
+    max-abs and max-rel (over |ref| > 1e-3) either way."""
     g = gpu_f16.astype(np.float64)
     assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
     err = np.abs(g - ref)
+    mabs, mrel = report(gpu_f16, ref)
+    print(f"{what}: max abs {mabs:.3g} max rel {mrel:.3g} (|ref| > 1e-3) over {err.size} elements"
+          f"{' [strict]' if strict else ''}")
+    if strict:
+        assert mabs <= ATOL, f"{what}: max abs err {mabs:.3g} above {ATOL} (strict bound)"
     bound = ATOL + RTOL * np.abs(ref)
     bad = err > bound
     if bad.any():

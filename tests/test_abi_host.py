@@ -55,6 +55,27 @@ def test_status_strings():
     assert kvfp8.status_str(99) == "KVFP8_UNKNOWN_STATUS"
 
 
+def test_attn_kernel_name_follows_the_launch_rule():
+    """The instantiation each attention call would launch (no launch; the
+    device's CU count is the 256 of an MI355X, also the fallback without a GPU)."""
+    name = kvfp8.kvfp8_attn_kernel_name
+    # decode: one workgroup per (sequence, kv-head, split) and the grid fits one round -> 8 wavefronts
+    assert name(32, 32, 4, 128, 16, 256, 1, 2) == "attn_split_kernel<128,16,1,8,false>"
+    # at most one 64-key tile per wavefront (splits of <= 512 keys) -> the short start-up
+    assert name(32, 8, 1, 128, 16, 256, 1, 8) == "attn_split_kernel<128,16,1,8,true>"
+    # more workgroups than compute units -> 4 wavefronts, two workgroups per CU
+    assert name(4, 32, 4, 128, 64, 4096, 1, 64) == "attn_split_kernel<128,64,1,4,false>"
+    # 32 query rows per kv-head (MTP3 at a GQA group of 8) -> two 16-row blocks
+    assert name(16, 32, 4, 128, 16, 2048, 4, 19) == "attn_split_kernel<128,16,2,4,false>"
+    # longer chunks -> the query-tiled chunk kernel (one split only)
+    assert name(1, 32, 4, 128, 16, 2004, 2048, 1) == "attn_chunk_kernel<128,16>"
+    assert name(1, 32, 4, 128, 16, 2004, 2048, 2) == ""
+    assert name(32, 32, 4, 128, 16, 256, 1, 2, True) == "attn_split_f16_kernel<128,16,1,8>"
+    assert name(1, 32, 4, 128, 16, 2004, 2048, 1, True) == ""
+    for bad in ((32, 32, 4, 96, 16, 256, 1, 2), (32, 30, 4, 128, 16, 256, 1, 2), (32, 32, 4, 128, 12, 256, 1, 2),
+                (0, 32, 4, 128, 16, 256, 1, 2), (32, 32, 4, 128, 16, 256, 1, 257)):
+        assert name(*bad) == "", bad
+
 def test_workspace_bytes():
     assert kvfp8.kvfp8_attn_workspace_bytes(32, 32, 128, 4) == 32 * 32 * 4 * 130 * 4
     assert kvfp8.kvfp8_attn_workspace_bytes(4, 32, 128, 64) == 4 * 32 * 64 * 130 * 4

@@ -1,7 +1,14 @@
 """GPU parity at the full sizes of the five workloads, in the launch
-configuration bench.py times (same split counts). Cache bytes and scales are
-compared bit for bit; attention outputs are compared on sampled sequences,
-which the oracle recomputes one by one, and checked finite everywhere.
+configuration bench.py times (same entry points, split counts and kernel
+instantiations). Cache bytes and scales are compared bit for bit; attention
+outputs are compared with the oracle on every sequence of the decode, MTP3 and
+mixed workloads and on two of the four 262,144-key sequences, each oracle row
+computed on its own.
+
+Tolerance: every N(0, 1) workload (tiny, 4k decode, MTP3, mixed layer) must
+meet max-abs <= 2e-3 outright besides the elementwise rule
+|err| <= 2e-3 + 1e-2 |ref|; the 256k workload, whose Student-t outlier channels
+put |ref| in the tens (one fp16 ulp above 2e-3), keeps the elementwise rule.
 """
 
 import numpy as np
@@ -11,7 +18,7 @@ import torch
 from oracle import calibrate_amax, paged_attention
 from synth import make_config
 from synth.workloads import make_mixed_calibration
-from tests.gpu_common import DeviceBatch, assert_close_attn, dev, oracle_caches, report
+from tests.gpu_common import DeviceBatch, assert_close_attn, dev, oracle_caches
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -47,6 +54,17 @@ def _write_all(K, bt, sc):
     return db
 
 
+def _write_prior(K, bt, sc):
+    """Caches holding every key but this step's new tokens, which the fused
+    steps append themselves."""
+    db = DeviceBatch(bt)
+    prior = dev(bt.prior_rows())
+    K.kv_quant_write(db.k[prior].contiguous(), db.v[prior].contiguous(), db.slots[prior].contiguous(),
+                     float(sc[0]), float(sc[1]), db.k_cache, db.v_cache)
+    new = dev(bt.new_token_rows())
+    return db, db.k[new].contiguous(), db.v[new].contiguous(), db.slots[new].contiguous()
+
+
 def _check_cache_bytes(db, bt, sc, rows=None):
     kc, vc = oracle_caches(bt, sc[0], sc[1], rows=rows)
     if rows is None:
@@ -69,6 +87,26 @@ def _decode(K, db, bt, sc, S):
     return out.cpu().numpy(), sm
 
 
+def _mtp3_splits(K, bt):
+    # the split count bench.py's MTP3 point uses
+    return K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
+                            n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
+
+
+def test_tiny_config_full(K):
+    """The tiny workload (batch 2, contexts 100 and 257, page 4, head_dim 64):
+    quantise-write every token, then attend, unsplit and split."""
+    bt = make_config(1)
+    sc = _scales_bit_exact(K, bt.k, bt.v)  # scales over the same tensors
+    db = _write_all(K, bt, sc)
+    kc, vc = _check_cache_bytes(db, bt, sc)
+    sm = np.float32(1.0 / np.sqrt(bt.head_dim))
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    for S in (1, 2, 5):
+        out, _ = _decode(K, db, bt, sc, S)
+        assert_close_attn(out, ref, f"tiny S={S}", strict=True)
+
+
 def test_decode_4k_full(K):
     bt = make_config(2)
     sc = _scales_bit_exact(K, bt.calib_k, bt.calib_v)
@@ -77,43 +115,94 @@ def test_decode_4k_full(K):
     assert ((kc & 0x7F) == 0x7E).any() and ((vc & 0x7F) == 0x7E).any()  # saturation exercised
     S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)
     out, sm = _decode(K, db, bt, sc, S)
-    assert np.isfinite(out.astype(np.float32)).all()
-    rows = [0, 13, 31]
-    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm, rows=rows)
-    assert_close_attn(out[rows], ref[rows], "decode 4k")
-    print("decode 4k S=%d max abs %.3g max rel %.3g" % ((S,) + report(out[rows], ref[rows])))
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"decode 4k S={S}, all 32 sequences", strict=True)
+
+
+def test_decode_append_4k_full_bench_step(K):
+    """The 4k decode step exactly as bench.py times it: the new token of each
+    of the 32 sequences appended by paged_attn_e4m3_decode_append at the
+    bench's split count, on the kernel instantiation the bench reports. Every
+    byte of the 128 MiB cache against the oracle's write of all tokens, all 32
+    rows against the oracle, and the fused step equal bit for bit to the write
+    kernel followed by decode."""
+    bt = make_config(2)
+    sc = _scales_bit_exact(K, bt.calib_k, bt.calib_v)
+    ks, vs = float(sc[0]), float(sc[1])
+    sm = float(np.float32(1.0 / np.sqrt(bt.head_dim)))
+    db, k_new, v_new, slots_new = _write_prior(K, bt, sc)
+    kc_sep, vc_sep = db.k_cache.clone(), db.v_cache.clone()
+    S = K.default_splits(bt.batch, bt.n_kv_heads, 4096)  # the bench's 4k split count
+    name = K.kvfp8_attn_kernel_name(bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.page_size,
+                                    bt.max_pages, 1, S)
+    print(f"4k decode step: S={S} kernel {name}")
+    assert name.startswith("attn_split_kernel<128,16,1,")
+    ws = K.workspace(bt.batch, bt.n_q_heads, bt.head_dim, S)
+    K.poison_partials(ws, bt.batch, bt.n_q_heads, bt.head_dim, S)
+    out = K.paged_attn_e4m3_decode_append(db.q, k_new, v_new, db.k_cache, db.v_cache, db.block_table,
+                                          db.seq_lens, ks, vs, sm, num_splits=S, workspace=ws).cpu().numpy()
+    kc, vc = _check_cache_bytes(db, bt, sc)  # all tokens, the appended ones included
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"decode_append 4k S={S} {name}, all 32 sequences", strict=True)
+    K.kv_quant_write(k_new, v_new, slots_new, ks, vs, kc_sep, vc_sep)
+    sep = K.paged_attn_e4m3_decode(db.q, kc_sep, vc_sep, db.block_table, db.seq_lens, ks, vs, sm, num_splits=S,
+                                   workspace=ws).cpu().numpy()
+    assert np.array_equal(out.view(np.uint16), sep.view(np.uint16))
 
 
 def test_mtp3_verify_full(K):
     bt = make_config(3)
     sc = _scales_bit_exact(K, bt.calib_k, bt.calib_v)
     db = _write_all(K, bt, sc)
-    longest = [int(np.argmax(bt.seq_lens)), int(np.argmin(bt.seq_lens))]
-    rows = sorted(set(longest + [5]))
-    kc, vc = _check_cache_bytes(db, bt, sc, rows=rows)
-    S = K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
-                                 n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
+    kc, vc = _check_cache_bytes(db, bt, sc)
+    S = _mtp3_splits(K, bt)
     sm = np.float32(1.0 / np.sqrt(bt.head_dim))
     ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S)
     K.poison_partials(ws, bt.total_q, bt.n_q_heads, bt.head_dim, S)
     out = K.paged_attn_e4m3_verify(db.q, db.cu_q, 4, db.k_cache, db.v_cache, db.block_table, db.seq_lens,
                                    float(sc[0]), float(sc[1]), float(sm), num_splits=S, workspace=ws)
     out = out.cpu().numpy()
-    assert np.isfinite(out.astype(np.float32)).all()
-    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm, rows=rows)
-    qrows = np.concatenate([np.arange(bt.cu_q_lens[b], bt.cu_q_lens[b + 1]) for b in rows])
-    assert_close_attn(out[qrows], ref[qrows], "mtp3 verify")
-    print("mtp3 S=%d contexts %s max abs %.3g max rel %.3g" % ((S, bt.seq_lens[rows].tolist()) +
-                                                              report(out[qrows], ref[qrows])))
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"mtp3 verify S={S}, all 16 sequences (contexts {sorted(set(bt.seq_lens.tolist()))})",
+                      strict=True)
+
+
+def test_verify_append_mtp3_full_bench_step(K):
+    """The MTP3 step exactly as bench.py times it: the four new tokens of each
+    of the 16 sequences appended by paged_attn_e4m3_verify_append at the bench's
+    split count. Every cache byte against the oracle, all 64 query rows against
+    the oracle, and the fused step equal bit for bit to write-then-verify."""
+    bt = make_config(3)
+    sc = _scales_bit_exact(K, bt.calib_k, bt.calib_v)
+    ks, vs = float(sc[0]), float(sc[1])
+    sm = float(np.float32(1.0 / np.sqrt(bt.head_dim)))
+    db, k_new, v_new, slots_new = _write_prior(K, bt, sc)
+    kc_sep, vc_sep = db.k_cache.clone(), db.v_cache.clone()
+    S = _mtp3_splits(K, bt)
+    mq = int(bt.q_lens.max())
+    name = K.kvfp8_attn_kernel_name(bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.page_size,
+                                    bt.max_pages, mq, S)
+    print(f"mtp3 step: S={S} kernel {name}")
+    ws = K.workspace(bt.total_q, bt.n_q_heads, bt.head_dim, S)
+    K.poison_partials(ws, bt.total_q, bt.n_q_heads, bt.head_dim, S)
+    out = K.paged_attn_e4m3_verify_append(db.q, k_new, v_new, db.cu_q, mq, db.k_cache, db.v_cache, db.block_table,
+                                          db.seq_lens, ks, vs, sm, num_splits=S, workspace=ws).cpu().numpy()
+    kc, vc = _check_cache_bytes(db, bt, sc)
+    ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
+    assert_close_attn(out, ref, f"verify_append mtp3 S={S} {name}, all 16 sequences", strict=True)
+    K.kv_quant_write(k_new, v_new, slots_new, ks, vs, kc_sep, vc_sep)
+    sep = K.paged_attn_e4m3_verify(db.q, db.cu_q, mq, kc_sep, vc_sep, db.block_table, db.seq_lens, ks, vs, sm,
+                                   num_splits=S, workspace=ws).cpu().numpy()
+    assert np.array_equal(out.view(np.uint16), sep.view(np.uint16))
 
 
 def test_long_context_256k_64_splits(K):
     bt = make_config(4)
     sc = _scales_bit_exact(K, bt.calib_k, bt.calib_v)
     db = _write_all(K, bt, sc)
-    del bt.k, bt.v  # the host copies are not needed any more beyond the sampled sequence
-    rows = [2]
-    bt2 = make_config(4)  # regenerate (seeded) for the oracle's own write of the sampled sequence
+    del bt.k, bt.v  # the host copies are regenerated (seeded) for the oracle's own write
+    rows = [0, 3]
+    bt2 = make_config(4)
     kc, vc = _check_cache_bytes(db, bt2, sc, rows=rows)
     pages = _sequence_pages(bt2, rows)
     sat = int(((kc[pages] & 0x7F) == 0x7E).sum() + ((vc[pages] & 0x7F) == 0x7E).sum())
@@ -122,9 +211,7 @@ def test_long_context_256k_64_splits(K):
     assert np.isfinite(out.astype(np.float32)).all()
     ref, _ = paged_attention(bt2.q, kc, vc, bt2.block_table, bt2.seq_lens, bt2.cu_q_lens, sc[0], sc[1], sm,
                              rows=rows)
-    assert_close_attn(out[rows], ref[rows], "256k")
-    print("256k S=64 saturated codes in sampled sequence %d, max abs %.3g max rel %.3g" %
-          ((sat,) + report(out[rows], ref[rows])))
+    assert_close_attn(out[rows], ref[rows], f"256k S=64 sequences {rows} ({sat} saturated codes)")
 
 
 def test_mixed_layer_full(K):
@@ -159,7 +246,5 @@ def test_mixed_layer_full(K):
                                      db.block_table[8:].contiguous(), db.seq_lens[8:].contiguous(),
                                      float(sc[0]), float(sc[1]), float(sm)).cpu().numpy()
     ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
-    assert_close_attn(dec, ref[:8], "mixed decode rows")
-    assert_close_attn(chunk, ref[8:], "mixed chunk rows")
-    print("mixed layer decode S=%d max abs %.3g / chunk max abs %.3g" %
-          (S, report(dec, ref[:8])[0], report(chunk, ref[8:])[0]))
+    assert_close_attn(dec, ref[:8], f"mixed decode rows S={S}", strict=True)
+    assert_close_attn(chunk, ref[8:], "mixed chunk rows (2,048 x 32 heads)", strict=True)

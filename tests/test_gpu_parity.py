@@ -243,7 +243,7 @@ def test_decode_parity(K, case, S):
     out = _run_decode(K, db, sc[0], sc[1], sm, S).cpu().numpy()
     kc, vc = oracle_caches(bt, sc[0], sc[1])
     ref, _ = paged_attention(bt.q, kc, vc, bt.block_table, bt.seq_lens, bt.cu_q_lens, sc[0], sc[1], sm)
-    assert_close_attn(out, ref, f"{case} S={S}")
+    assert_close_attn(out, ref, f"{case} S={S}", strict=(case == "tiny"))
 
 
 APPEND_CASES = {
@@ -251,6 +251,9 @@ APPEND_CASES = {
     "d128_p16": lambda: make_batch([1, 16, 17, 64, 65, 300], [1] * 6, 32, 4, 128, 16, seed=57),
     "d64_p8": lambda: make_batch([9, 130, 8], [1] * 3, 16, 4, 64, 8, seed=58),
     "d128_p64_g4": lambda: make_batch([700, 64, 129], [1] * 3, 16, 4, 128, 64, seed=59),
+    # contexts longer than 512 keys per split at page 16: several tiles per wavefront (the
+    # instantiation the 4k decode step runs, not the short start-up)
+    "d128_p16_long": lambda: make_batch([3000, 1500, 2049, 700, 1], [1] * 5, 32, 4, 128, 16, seed=60),
 }
 
 
@@ -263,6 +266,10 @@ def test_decode_append_equals_write_then_decode(K, case, S):
     bt = APPEND_CASES[case]()
     _, sc = oracle_scales(bt)
     ks, vs, sm = float(sc[0]), float(sc[1]), float(sm_of(bt))
+    name = K.kvfp8_attn_kernel_name(bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.page_size,
+                                    bt.max_pages, 1, S)
+    if case == "d128_p16_long":
+        assert name == "attn_split_kernel<128,16,1,8,false>", name
     db = DeviceBatch(bt)
     prior, new = dev(bt.prior_rows()), dev(bt.new_token_rows())
     K.kv_quant_write(db.k[prior].contiguous(), db.v[prior].contiguous(), db.slots[prior].contiguous(), ks, vs,
