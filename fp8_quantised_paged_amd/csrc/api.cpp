@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "../../include/kvfp8.h"
@@ -185,6 +186,56 @@ int32_t run_attention(const AttnCommon& c, const int32_t* cu_q, int64_t n_rows, 
 
 }  // namespace
 
+// ------------------------------------------------------------ static scratch
+// The FP32 split workspace of paged_attn_e4m3_decode_append_noalloc, for
+// callers that cannot allocate: a file-scope device array of
+// KVFP8_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: only
+// the address hipGetSymbolAddress returns for the current device may reach a
+// kernel.
+static __device__ __align__(256) float scratch[KVFP8_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device with that device current and kept.
+int32_t device_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(KVFP8_UNSUPPORTED, "device %d: the scratch table holds devices 0..%d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(KVFP8_HIP_ERROR, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return KVFP8_OK;
+}
+
+// Host checks of a decode step with appended tokens (the arguments of
+// paged_attn_e4m3_decode_append).
+int32_t check_decode_append(const AttnCommon& c, const uint16_t* k_new, const uint16_t* v_new) {
+  int32_t st = check_common(c, c.batch);
+  if (st != KVFP8_OK) return st;
+  if (c.n_q_heads / c.n_kv_heads > kSplitRows)
+    return fail(KVFP8_UNSUPPORTED, "GQA group of %d heads (at most %d)", c.n_q_heads / c.n_kv_heads, kSplitRows);
+  if (c.batch > 0 && (!k_new || !v_new)) return fail(KVFP8_INVALID_ARG, "null new-token pointer");
+  if (c.batch > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(KVFP8_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  return KVFP8_OK;
+}
+
+}  // namespace
+
 KVFP8_API const char* kvfp8_status_str(int32_t status) {
   switch (status) {
     case KVFP8_OK: return "KVFP8_OK";
@@ -322,14 +373,42 @@ KVFP8_API int32_t paged_attn_e4m3_decode_append(const uint16_t* q_f16, const uin
   AttnCommon c{q_f16, k_cache, v_cache, block_table, seq_lens, batch, n_q_heads, n_kv_heads,
                head_dim, page_size, max_pages_per_seq, k_scale, v_scale, sm_scale, num_splits,
                workspace, workspace_bytes, out_f16};
-  int32_t st = check_common(c, batch);
+  int32_t st = check_decode_append(c, k_new, v_new);
   if (st != KVFP8_OK) return st;
-  if (n_q_heads / n_kv_heads > kSplitRows)
-    return fail(KVFP8_UNSUPPORTED, "GQA group of %d heads (at most %d)", n_q_heads / n_kv_heads,
-                kSplitRows);
-  if (batch > 0 && (!k_new || !v_new)) return fail(KVFP8_INVALID_ARG, "null new-token pointer");
-  if (batch > 0 && (!aligned16(k_new) || !aligned16(v_new)))
-    return fail(KVFP8_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  const AppendArgs app{k_new, v_new, k_cache, v_cache};
+  return run_attention(c, nullptr, batch, 1, stream, &app);
+}
+
+KVFP8_API int32_t paged_attn_e4m3_decode_append_noalloc(const uint16_t* q_f16, const uint16_t* k_new,
+                                                        const uint16_t* v_new, uint8_t* k_cache, uint8_t* v_cache,
+                                                        const int32_t* block_table, const int32_t* seq_lens,
+                                                        int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                                        int32_t head_dim, int32_t page_size,
+                                                        int32_t max_pages_per_seq, float k_scale, float v_scale,
+                                                        float sm_scale, int32_t num_splits, uint16_t* out_f16,
+                                                        hipStream_t stream) {
+  if (!out_f16) return fail(KVFP8_INVALID_ARG, "out must not be NULL (the partials stay in the library's scratch)");
+  const bool split = num_splits > 1;
+  if (split && batch > 0 && n_q_heads > 0 && head_dim > 0) {
+    const size_t need = kvfp8_attn_workspace_bytes(batch, n_q_heads, head_dim, num_splits);
+    if (need > (size_t)KVFP8_NOALLOC_SCRATCH_BYTES)
+      return fail(KVFP8_WORKSPACE, "the split partials need %zu bytes; the static scratch holds %zu "
+                  "(fewer splits, a smaller batch, or paged_attn_e4m3_decode_append with a workspace)",
+                  need, (size_t)KVFP8_NOALLOC_SCRATCH_BYTES);
+  }
+  // every argument is checked on the host, with the scratch standing in for
+  // the workspace, before the first HIP call
+  float* const kStandIn = reinterpret_cast<float*>(uintptr_t{256});
+  AttnCommon c{q_f16, k_cache, v_cache, block_table, seq_lens, batch, n_q_heads, n_kv_heads,
+               head_dim, page_size, max_pages_per_seq, k_scale, v_scale, sm_scale, num_splits,
+               split ? kStandIn : nullptr, split ? (size_t)KVFP8_NOALLOC_SCRATCH_BYTES : 0, out_f16};
+  int32_t st = check_decode_append(c, k_new, v_new);
+  if (st != KVFP8_OK) return st;
+  if (batch == 0) return ok();
+  if (split) {
+    st = device_scratch(&c.workspace);
+    if (st != KVFP8_OK) return st;
+  }
   const AppendArgs app{k_new, v_new, k_cache, v_cache};
   return run_attention(c, nullptr, batch, 1, stream, &app);
 }

@@ -25,6 +25,7 @@ EXPORTED = (
     "kv_quant_write",
     "paged_attn_e4m3_decode",
     "paged_attn_e4m3_decode_append",
+    "paged_attn_e4m3_decode_append_noalloc",
     "paged_attn_e4m3_verify",
     "paged_attn_e4m3_verify_append",
     "paged_attn_f16_decode",
@@ -65,6 +66,8 @@ def _load() -> ctypes.CDLL:
                                          I32, P, SZ, P, P]),
         "paged_attn_e4m3_decode_append": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32,
                                                 F32, F32, I32, P, SZ, P, P]),
+        "paged_attn_e4m3_decode_append_noalloc": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                                        F32, F32, F32, I32, P, P]),
         "paged_attn_e4m3_verify": (I32, [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                          F32, F32, F32, I32, P, SZ, P, P]),
         "paged_attn_e4m3_verify_append": (I32, [P, P, P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32,
@@ -332,6 +335,37 @@ def paged_attn_e4m3_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
            "paged_attn_e4m3_decode_append")
     return out
 
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVFP8_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attn_e4m3_decode_append_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                          k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                                          seq_lens: torch.Tensor, k_scale: float, v_scale: float, sm_scale: float,
+                                          num_splits: int = 1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attn_e4m3_decode_append with the split partials in the library's static per-GPU scratch
+    (the C call allocates nothing; pass `out` to allocate nothing here either). Returns out."""
+    _need(q, "q", torch.float16, 3)
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, hq, d = q.shape
+    hkv, psz, _ = _cache_dims(k_cache, v_cache, d)
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{B}, {hkv}, {d}]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16, 3)
+    _check_rows("paged_attn_e4m3_decode_append_noalloc", out, q, block_table, seq_lens, B, None)
+    _check(_lib.paged_attn_e4m3_decode_append_noalloc(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                                      k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                                      seq_lens.data_ptr(), B, hq, hkv, d, psz, block_table.shape[1],
+                                                      float(k_scale), float(v_scale), float(sm_scale),
+                                                      int(num_splits), out.data_ptr(), _stream()),
+           "paged_attn_e4m3_decode_append_noalloc")
+    return out
 
 def paged_attn_e4m3_verify(q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
                            k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

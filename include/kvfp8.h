@@ -177,6 +177,34 @@ int32_t paged_attn_e4m3_decode_append(const uint16_t* q_f16, const uint16_t* k_n
                                       int32_t num_splits, float* workspace, size_t workspace_bytes,
                                       uint16_t* out_f16, hipStream_t stream);
 
+/* Bytes of the library's static FP32 scratch used by
+ * paged_attn_e4m3_decode_append_noalloc: one copy per GPU the library runs on,
+ * held until the process ends. */
+#define KVFP8_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the decode step of
+ * paged_attn_e4m3_decode_append with the FP32 split partials kept in the
+ * library's static per-GPU scratch (KVFP8_NOALLOC_SCRATCH_BYTES) instead of a
+ * caller workspace. Same arguments, kernels, results and errors as
+ * paged_attn_e4m3_decode_append without workspace and workspace_bytes; out_f16
+ * must not be NULL. The call allocates nothing (no hipMalloc, no library
+ * allocation); its first call on a device looks up that device's scratch
+ * address. Returns KVFP8_WORKSPACE, before any HIP call, when num_splits > 1
+ * needs more than KVFP8_NOALLOC_SCRATCH_BYTES, i.e. when
+ * kvfp8_attn_workspace_bytes(batch, n_q_heads, head_dim, num_splits) exceeds it.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * partials (each call writes every partial it reads, so nothing needs
+ * clearing): calls on one GPU must not overlap (issue them on one stream, or
+ * order them), or they race. */
+int32_t paged_attn_e4m3_decode_append_noalloc(const uint16_t* q_f16, const uint16_t* k_new, const uint16_t* v_new,
+                                              uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
+                                              const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                              int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                              int32_t max_pages_per_seq, float k_scale, float v_scale,
+                                              float sm_scale, int32_t num_splits, uint16_t* out_f16,
+                                              hipStream_t stream);
+
 /* Multi-query attention with a causal mask among each sequence's query tokens:
  * MTP verify of 1 + drafted tokens ([P1] Purpose and Validation on 4xV100 TP4:
  * MTP3 verifies up to four tokens per step) and prefill/catch-up chunks in mixed

@@ -76,6 +76,28 @@ def test_attn_kernel_name_follows_the_launch_rule():
                 (0, 32, 4, 128, 16, 256, 1, 2), (32, 32, 4, 128, 16, 256, 1, 257)):
         assert name(*bad) == "", bad
 
+def test_decode_append_noalloc_rejects_before_any_hip_call():
+    """The entry point without a workspace refuses split partials larger than its
+    static scratch (KVFP8_WORKSPACE) and a NULL output, before touching the GPU."""
+    f = L.paged_attn_e4m3_decode_append_noalloc
+    base = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, B=64, hq=32, hkv=4, d=128, p=16,
+                mp=64, ks=1.0, vs=1.0, sm=0.1, S=128, out=FAKE)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["sl"], a["B"], a["hq"], a["hkv"], a["d"],
+                 a["p"], a["mp"], a["ks"], a["vs"], a["sm"], a["S"], a["out"], None)
+
+    assert kvfp8.kvfp8_attn_workspace_bytes(64, 32, 128, 128) > kvfp8.NOALLOC_SCRATCH_BYTES
+    assert call() == kvfp8.WORKSPACE
+    assert "static scratch" in kvfp8.last_error()
+    assert call(out=None) == kvfp8.INVALID_ARG
+    assert call(S=2, ks=float("nan")) == kvfp8.BAD_SCALE
+    assert call(S=2, d=96) == kvfp8.UNSUPPORTED
+    assert call(S=2, kn=None) == kvfp8.INVALID_ARG
+    assert call(S=2, q=MIS) == kvfp8.INVALID_ARG
+    assert call(B=0, S=2) == kvfp8.OK
+
 def test_workspace_bytes():
     assert kvfp8.kvfp8_attn_workspace_bytes(32, 32, 128, 4) == 32 * 32 * 4 * 130 * 4
     assert kvfp8.kvfp8_attn_workspace_bytes(4, 32, 128, 64) == 4 * 32 * 64 * 130 * 4
