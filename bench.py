@@ -444,6 +444,30 @@ class MixedLayer:
 
 
 
+def dense_f16_gemm_rate(torch, n=8192, launches=20):
+    """Achievable dense fp16 matrix-core rate on this GPU: torch.mm of two
+    contiguous n x n fp16 matrices (the vendor GEMM library), HIP events around
+    a graph of back-to-back products. A reference for the chunk kernel's
+    matrix-core rate beside the 2.5 PFLOP/s datasheet figure."""
+    a = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    c = torch.empty((n, n), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / launches
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"tflops": 2.0 * n ** 3 / sec / 1e12, "n": n, "us": sec * 1e6,
+            "method": f"torch.mm fp16 {n}x{n}x{n}, mean of {launches} back-to-back launches"}
+
+
 def cpu_baseline(seconds_target=10.0):
     """The fp64 oracle timed on host cores over sampled sequences of the 4k
     decode workload (same seeded inputs as the GPU run)."""
@@ -640,9 +664,9 @@ def main():
             k_src = normal_kv(total, 4, 128, bt.seed * 10 + 1)
             v_src = normal_kv(total, 4, 128, bt.seed * 10 + 2)
             calib = None
-            S = (K.default_splits(bt.batch, bt.n_kv_heads, 4096) if p == "4k_f16" else
+            S = (K.default_splits(bt.batch, bt.n_kv_heads, 4096, kv_elem_bytes=2) if p == "4k_f16" else
                  K.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
-                                 n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max())))
+                                  n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()), kv_elem_bytes=2))
             nsets, steps = (6, args.steps) if p == "4k_f16" else (3, max(10, args.steps // 3))
         elif p == "mtp3":
             bt = make_config(3)
@@ -667,6 +691,9 @@ def main():
             del calib
             ml = MixedLayer(K, torch, scales)
             r = ml.time(max(10, args.steps // 3))
+            gemm = dense_f16_gemm_rate(torch)
+            r["dense_f16_gemm_reference"] = gemm
+            r["chunk_frac_of_dense_gemm_rate"] = r["chunk_tflops"] / gemm["tflops"]
             r["calibration_us_48_tensors_host_inclusive"] = cal_us
             r["calibration_gbs"] = 48 * 4096 * 512 * 2 / (cal_us * 1e-6) / 1e9
             results[p] = r

@@ -161,15 +161,24 @@ def kvfp8_attn_kernel_name(batch: int, n_q_heads: int, n_kv_heads: int, head_dim
     return _lib.kvfp8_attn_kernel_name(batch, n_q_heads, n_kv_heads, head_dim, page_size, max_pages_per_seq,
                                        max_q_len, num_splits, int(bool(f16_kv))).decode()
 
+VERIFY_ONE_PER_CU_BYTES = 1.2e6  # KV bytes per compute unit up to which verify runs one workgroup per CU
+
+
 def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Optional[int] = None,
-                   cus: int = 256, seq_lens=None, n_q_heads: Optional[int] = None, q_len: int = 1) -> int:
+                   cus: int = 256, seq_lens=None, n_q_heads: Optional[int] = None, q_len: int = 1,
+                   head_dim: int = 128, kv_elem_bytes: int = 1) -> int:
     """Split count for the split kernel (host-side heuristic).
 
-    Aims for one round of equal-work workgroups over the compute units: the
-    kernel runs one workgroup per CU when a kv-head has at most 16 query rows
-    (q_len times the GQA group n_q_heads / n_kv_heads; decode, unless the group
-    exceeds 16) and two otherwise. All sequences of a call share one split
-    size, set by the longest context and the split count, so a shorter
+    Aims for one round of equal-work workgroups over the compute units. Decode
+    (at most 16 query rows per kv-head: q_len times the GQA group n_q_heads /
+    n_kv_heads) runs 8-wavefront workgroups, one per CU. Verify runs
+    4-wavefront workgroups: one per CU while the call's KV bytes (keys x
+    n_kv_heads x head_dim x 2 x kv_elem_bytes) stay within
+    VERIFY_ONE_PER_CU_BYTES per CU, where start-up and tail dominate, and two
+    per CU above it, where the bytes they keep in flight pay off (measured on the
+    MTP3 workload: 0.83 MB per CU over E4M3 pages runs fastest at one per CU,
+    1.66 MB per CU over fp16 pages at two). All sequences of a call share one
+    split size, set by the longest context and the split count, so a shorter
     sequence fills fewer splits. With the context lengths known on the host
     (seq_lens), this returns the split count with the most non-empty splits,
     over all sequences and kv-heads, that still fit in those slots (the
@@ -179,7 +188,11 @@ def default_splits(batch: int, n_kv_heads: int, max_seq_len: int, total_keys: Op
     is only one); at most 256 splits."""
     heads = max(1, n_kv_heads)
     group = (n_q_heads // heads) if n_q_heads else 1
-    slots = (1 if q_len * group <= 16 else 2) * cus
+    keys = (sum(int(x) for x in seq_lens) if seq_lens is not None
+            else (total_keys if total_keys is not None else batch * max_seq_len))
+    kv_bytes = keys * heads * head_dim * 2 * kv_elem_bytes
+    verify = q_len * group > 16
+    slots = 2 * cus if (verify and kv_bytes > VERIFY_ONE_PER_CU_BYTES * cus) else cus
     if seq_lens is not None:
         lens = [int(x) for x in seq_lens]
         lmax = max(lens) if lens else 0

@@ -17,8 +17,10 @@ def items(lens, heads, S):
     return heads * sum(sum(1 for a, b in split_bounds(L, S, 64, lmax) if b > a) for L in lens if L > 0)
 
 
-def slots(cus, rows):
-    return (1 if rows <= 16 else 2) * cus
+def slots(cus, rows, lens, heads, head_dim=128, elem=1):
+    # decode: one workgroup per CU; verify: one per CU up to 1.2 MB of KV per CU, two above
+    kv = sum(lens) * heads * head_dim * 2 * elem
+    return 2 * cus if (rows > 16 and kv > 1.2e6 * cus) else cus
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -32,7 +34,7 @@ def test_ragged_choice_is_the_fullest_that_fits(seed):
     lens[0] = max(lens[0], 1)
     cus = int(rng.choice([64, 256]))
     S = kvfp8.default_splits(B, heads, max(lens), cus=cus, seq_lens=lens, n_q_heads=heads * group, q_len=q_len)
-    cap = slots(cus, q_len * group)
+    cap = slots(cus, q_len * group, lens, heads)
     lmax = max(lens)
     assert 1 <= S <= 256
     if S > 1:
@@ -63,7 +65,11 @@ def test_mtp3_workload_split_count():
     S = kvfp8.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
                              n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()))
     lens = [int(x) for x in bt.seq_lens]
-    assert S == 19 and items(lens, bt.n_kv_heads, S) == 496  # 496 items over 512 slots (2 per CU)
+    assert S == 8 and items(lens, bt.n_kv_heads, S) == 220  # 0.83 MB per CU: 220 items over 256 slots (1 per CU)
+    # the same workload over fp16 pages: 1.66 MB per CU, two workgroups per CU
+    S16 = kvfp8.default_splits(bt.batch, bt.n_kv_heads, int(bt.seq_lens.max()), seq_lens=bt.seq_lens,
+                               n_q_heads=bt.n_q_heads, q_len=int(bt.q_lens.max()), kv_elem_bytes=2)
+    assert S16 == 19 and items(lens, bt.n_kv_heads, S16) == 496
 
 
 def test_empty_batch_and_zero_lengths():
