@@ -247,7 +247,7 @@ constexpr float kLazy = 8.0f;
 template <int D, int P, int NB, bool QREG>
 __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, int g,
                                              const f16x8 (*sq)[D / 32][64], const f16x8 (&qreg)[NB][D / 32],
-                                             const int (&lim)[NB],
+                                             const int (&lim)[NB], bool masked,
                                              float score_scale, float (&m_ref)[NB], float (&m_max)[NB],
                                              float (&l_run)[NB], f32x4 (&o)[NB][D / 16]) {
   constexpr int NBLK = D / 16;
@@ -298,8 +298,9 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, P>& r, int t0, int L, i
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     // mask keys at or past each row's limit (the end of the split, or the
-    // row's causal position); the compare constants are the lane's key offsets
-    {
+    // row's causal position); the compare constants are the lane's key offsets.
+    // Tiles below every row's limit skip it (masked is wave-uniform).
+    if (masked) {
       const int rem = lim[nb] - t0 - 16 * g;  // keys 16g + k of the tile with k < rem are visible
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -406,6 +407,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   const int start = s * itm.chunk;
   const int end = min(start + itm.chunk, L);
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
+  // the smallest limit over the query rows (row i of the sequence sees keys
+  // below min(end, L - T + i + 1)): tiles that end at or below it need no mask
+  const int mask_from = min(end, L - T + 1);
   // the sequence's last item also marks its unused split slots as empty
   // (m = -inf, l = 0: weight zero in the reduce, which never multiplies their o)
   const int s_fill_end = (s == itm.n_used - 1) ? S : s + 1;
@@ -562,12 +566,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
       while (true) {
         load_pages<P>(pa, btrow, start + (it + 2 * W) * kTile, last, n, g);
         if (it + W < ntiles) load_tile<D, P>(rb, pb, lo, kbase, vbase, page_stride);
-        compute_tile<D, P, NB, false>(ra, start + it * kTile, L, g, sm_q, qraw, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_tile<D, P, NB, false>(ra, start + it * kTile, L, g, sm_q, qraw, lim,
+                               start + (it + 1) * kTile > mask_from, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
         load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
         if (it + W < ntiles) load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
-        compute_tile<D, P, NB, false>(rb, start + it * kTile, L, g, sm_q, qraw, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_tile<D, P, NB, false>(rb, start + it * kTile, L, g, sm_q, qraw, lim,
+                               start + (it + 1) * kTile > mask_from, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
       }
@@ -592,7 +598,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
       if (it + W < ntiles) load_tile_lds<D, P>(tb, pb, lo, kbase, vbase, page_stride);
       while (true) {
         load_pages<P>(pb, btrow, start + (it + 2 * W) * kTile, last, n, g);
-        compute_tile<D, P, NB, true>(ra, start + it * kTile, L, g, nullptr, qraw, lim, a.score_scale, m_ref, m_max, l_run,
+        compute_tile<D, P, NB, true>(ra, start + it * kTile, L, g, nullptr, qraw, lim,
+                               start + (it + 1) * kTile > mask_from, a.score_scale, m_ref, m_max, l_run,
                                o);
         it += W;
         if (it >= ntiles) break;
@@ -607,7 +614,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
     if (it < ntiles) {
       while (true) {
         load_pages<P>(pb, btrow, start + (it + W) * kTile, last, n, g);
-        compute_tile<D, P, NB, false>(ra, start + it * kTile, L, g, sm_q, qraw, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_tile<D, P, NB, false>(ra, start + it * kTile, L, g, sm_q, qraw, lim,
+                               start + (it + 1) * kTile > mask_from, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
         load_tile<D, P>(ra, pb, lo, kbase, vbase, page_stride);

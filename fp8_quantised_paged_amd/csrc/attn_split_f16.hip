@@ -93,7 +93,7 @@ __device__ __forceinline__ void load_f16(TileF16<D>& r, const PagesF16& pg, int 
 
 template <int D, int NB>
 __device__ __forceinline__ void compute_f16(TileF16<D>& r, int t0, int L, int g, const f16x8 (*sq)[D / 32][64],
-                                            const int (&lim)[NB], float score_scale, float (&m_ref)[NB],
+                                            const int (&lim)[NB], bool masked, float score_scale, float (&m_ref)[NB],
                                             float (&m_max)[NB], float (&l_run)[NB], f32x4 (&o)[NB][D / 16]) {
   constexpr int NBLK = D / 16;
   // keys at or past the end of the sequence may hold anything, NaN included:
@@ -134,12 +134,15 @@ __device__ __forceinline__ void compute_f16(TileF16<D>& r, int t0, int L, int g,
   f16x8 pk[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int rem = lim[nb] - t0 - 8 * g;  // keys 8g + j of the tile with j < rem are visible
+    // tiles below every row's limit skip the mask (masked is wave-uniform)
+    if (masked) {
+      const int rem = lim[nb] - t0 - 8 * g;  // keys 8g + j of the tile with j < rem are visible
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * t + i >= rem) sc[t][nb][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i)
+          if (4 * t + i >= rem) sc[t][nb][i] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -233,7 +236,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
   }
 
   // ---- Q operand (dims g*D/4 + 8c + i of row n of each 16-row block) and
-  // each row's visible-key limit
+  // each row's visible-key limit; tiles that end at or below the smallest
+  // limit over the query rows, min(end, L - T + 1), need no mask
+  const int mask_from = min(end, L - T + 1);
   f16x8 qb[NB][NC];
   int lim[NB];
 #pragma unroll
@@ -296,12 +301,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
       while (true) {
         pages_f16<P>(pa, btrow, start + (it + 2 * W) * kTileF, last, n, g);
         if (it + W < ntiles) load_f16<D, P>(rb, pb, start + (it + W) * kTileF, n, g, kbase, vbase, page_bytes);
-        compute_f16<D, NB>(ra, start + it * kTileF, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_f16<D, NB>(ra, start + it * kTileF, L, g, sm_q, lim,
+                           start + (it + 1) * kTileF > mask_from, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
         pages_f16<P>(pb, btrow, start + (it + 2 * W) * kTileF, last, n, g);
         if (it + W < ntiles) load_f16<D, P>(ra, pa, start + (it + W) * kTileF, n, g, kbase, vbase, page_bytes);
-        compute_f16<D, NB>(rb, start + it * kTileF, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_f16<D, NB>(rb, start + it * kTileF, L, g, sm_q, lim,
+                           start + (it + 1) * kTileF > mask_from, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
       }
@@ -312,7 +319,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
     // its page ids already loaded
     if (it < ntiles) {
       while (true) {
-        compute_f16<D, NB>(ra, start + it * kTileF, L, g, sm_q, lim, a.score_scale, m_ref, m_max, l_run, o);
+        compute_f16<D, NB>(ra, start + it * kTileF, L, g, sm_q, lim,
+                           start + (it + 1) * kTileF > mask_from, a.score_scale, m_ref, m_max, l_run, o);
         it += W;
         if (it >= ntiles) break;
         load_f16<D, P>(ra, pb, start + it * kTileF, n, g, kbase, vbase, page_bytes);
