@@ -39,11 +39,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # FETCH_SIZE / WRITE_SIZE runs (`bench.py --counter-pass`), scaled by the same
 # counters' reading of a 1 GiB device copy. Valid only for the kernel source
 # they were taken on (sha256 prefix); otherwise the traffic is reported as null.
-MEASURED_TRAFFIC = {"source_sha256_prefix": "6b6538fb3ba26211", "read_bytes": 136757704,
+MEASURED_TRAFFIC = {"source_sha256_prefix": "05f735e96dd5d063", "read_bytes": 136857030,
                     "write_bytes": 1081344}
 
 
-TRAFFIC_SOURCES = ("attn_split.hip", "split_plan.h")  # the sources the counted kernel is built from
+TRAFFIC_SOURCES = ("attn_split.hip", "split_plan.h", "kvfp8_internal.h")  # the sources the counted kernel is built from
 
 
 def measured_traffic():
