@@ -418,10 +418,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_chunk_kernel(const AttnArgs 
     const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
     chunk_load<D, P>(regs, pg, tid, (t + 2) * kTile, kbase, vbase, page_stride);
     chunk_pages<D, P>(pg, tid, (t + 3) * kTile, last, btrow);
-    chunk_qk<D>(sm, buf1, n, g, qb, nxt);
-    chunk_softmax<D, MASKED>(cur, t * kTile, g, lim, a.score_scale, m_ref, m_max, lacc, o, pk);
-    chunk_pv<D>(sm, buf, n, g, pk, lacc, o);
-    chunk_store<D>(sm, buf2, regs, tid, (t + 2) * kTile, L);
+    // The per-tile barrier keeps every wavefront on the same tile. The two
+    // wavefronts that share a SIMD (w and w + 4) take that tile's steps in
+    // opposite orders, matrix core first against vector ALU first, so the
+    // SIMD has one wavefront in each kind of work more of the time. Each
+    // wavefront's own arithmetic is the same in both orders.
+    if (wave < kWaves / 2) {
+      chunk_qk<D>(sm, buf1, n, g, qb, nxt);
+      chunk_softmax<D, MASKED>(cur, t * kTile, g, lim, a.score_scale, m_ref, m_max, lacc, o, pk);
+      chunk_pv<D>(sm, buf, n, g, pk, lacc, o);
+      chunk_store<D>(sm, buf2, regs, tid, (t + 2) * kTile, L);
+    } else {
+      chunk_softmax<D, MASKED>(cur, t * kTile, g, lim, a.score_scale, m_ref, m_max, lacc, o, pk);
+      chunk_qk<D>(sm, buf1, n, g, qb, nxt);
+      chunk_store<D>(sm, buf2, regs, tid, (t + 2) * kTile, L);
+      chunk_pv<D>(sm, buf, n, g, pk, lacc, o);
+    }
     __syncthreads();
     buf = buf1;
   };
