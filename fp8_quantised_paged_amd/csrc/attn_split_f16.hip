@@ -11,9 +11,10 @@
 // tile, and the same two-tile register pipeline fits. Key permutation over the
 // tile's two 16-key M-tiles: MFMA row m of M-tile t is key 8(m/4) + 4t + m%4,
 // so lane group g's accumulators hold keys 8g .. 8g+7 of every query row, in
-// order: the B operand of the PV product as it stands. Dimensions follow the
-// E4M3 kernel's order (lane group g holds dims g*D/4 .. g*D/4 + D/4 - 1 of its
-// key row, and the Q operand matches).
+// order: the B operand of the PV product as it stands. Dimensions: QK chunk c
+// of lane group g covers dims 32c + 8g .. 32c + 8g + 7, so each 16-byte load
+// instruction reads 64 contiguous bytes of every key row; the Q operand
+// matches.
 #include <cstdio>
 
 #include "kvfp8_internal.h"
@@ -39,7 +40,7 @@ __device__ __forceinline__ float group_sum(float x) {
 
 template <int D>
 struct TileF16 {
-  u32x4 k[2][D / 32];  // M-tile t: dims g*D/4 .. +D/4-1 of key row 8(n/4) + 4t + n%4
+  u32x4 k[2][D / 32];  // M-tile t, chunk c: dims 32c + 8g .. +7 of key row 8(n/4) + 4t + n%4
   u32x4 v[D / 16];     // dim block blk: keys 8g .. 8g+7 of dim 16*blk + n
 };
 
@@ -65,13 +66,17 @@ template <int D, int P>
 __device__ __forceinline__ void load_f16(TileF16<D>& r, const PagesF16& pg, int t0, int n, int g,
                                          const uint8_t* __restrict__ kbase, const uint8_t* __restrict__ vbase,
                                          uint32_t page_bytes) {
+  // The contraction order over dims is free: chunk c of lane group g holds
+  // dims 32c + 8g .. +7, so each load instruction reads 64 contiguous bytes of
+  // every key row (the four lane groups side by side), not four 16-byte pieces
+  // 64 bytes apart. Q uses the same order.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int off = (t0 + 8 * (n >> 2) + 4 * t + (n & 3)) % P;
     const u32x4* p = reinterpret_cast<const u32x4*>(kbase + (uint64_t)(uint32_t)pg.k[t] * page_bytes +
-                                                    (uint32_t)(2 * (off * D + (D / 4) * g)));
+                                                    (uint32_t)(2 * (off * D + 8 * g)));
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) r.k[t][j] = __builtin_nontemporal_load(p + j);
+    for (int j = 0; j < D / 32; ++j) r.k[t][j] = __builtin_nontemporal_load(p + 4 * j);
   }
 #pragma unroll
   for (int blk = 0; blk < D / 16; ++blk) {
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
     return;
   }
 
-  // ---- Q operand (dims g*D/4 + 8c + i of row n of each 16-row block) and
+  // ---- Q operand (dims 32c + 8g + i of row n of each 16-row block) and
   // each row's visible-key limit; tiles that end at or below the smallest
   // limit over the query rows, min(end, L - T + 1), need no mask
   const int mask_from = min(end, L - T + 1);
@@ -247,9 +252,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_f16_kernel(const AttnArg
     const int i = rr / G;
     lim[nb] = rr < nrows ? min(end, L - T + i + 1) : 0;
     if (rr < nrows) {
-      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + kvh * G + rr % G) * D + (D / 4) * g;
+      const uint16_t* qp = a.q + ((int64_t)(q0 + i) * a.n_q_heads + kvh * G + rr % G) * D + 8 * g;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 8 * c);
+      for (int c = 0; c < NC; ++c) qb[nb][c] = *reinterpret_cast<const f16x8*>(qp + 32 * c);
     } else {
 #pragma unroll
       for (int c = 0; c < NC; ++c) qb[nb][c] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
