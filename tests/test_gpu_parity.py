@@ -131,6 +131,8 @@ def _slot_pattern(kind, P, num_pages, rng):
         return rng.permutation(cap)[:300]
     if kind == "scattered_small":  # a decode step's size
         return rng.permutation(cap)[:100]
+    if kind == "scattered_large":  # single scattered slots in a call large enough for looping workgroups
+        return rng.permutation(cap)[:20000]
     if kind == "runs":  # contiguous runs from arbitrary starts, in random order
         runs, used = [], set()
         while len(runs) < 12:
@@ -152,7 +154,8 @@ def _slot_pattern(kind, P, num_pages, rng):
     return np.concatenate(out)
 
 
-@pytest.mark.parametrize("kind", ["scattered_small", "scattered", "runs", "runs_with_holes", "paged", "paged_large"])
+@pytest.mark.parametrize("kind", ["scattered_small", "scattered", "runs", "runs_with_holes", "paged", "paged_large",
+                                  "scattered_large"])
 @pytest.mark.parametrize("D,P", [(128, 4), (128, 16), (128, 64), (64, 8), (64, 32)])
 def test_quant_write_slot_patterns(K, kind, D, P):
     """The write stores V in runs of consecutive slots, aligned quads and single
@@ -160,7 +163,7 @@ def test_quant_write_slot_patterns(K, kind, D, P):
     tokens; fewer than about four workgroups per CU; more): every slot pattern
     and size gives the oracle's cache bytes exactly."""
     rng = np.random.default_rng([sum(map(ord, kind)), D, P])
-    if kind == "paged_large":  # about 24,000 tokens over 8 kv-heads: the large-call shape
+    if kind in ("paged_large", "scattered_large"):  # 20,000-24,000 tokens over 8 kv-heads: the large-call shape
         num_pages, hkv = 48000 // P + 8, 8
     else:
         num_pages, hkv = 3000 // P + 8, 2
