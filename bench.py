@@ -510,7 +510,8 @@ def cpu_baseline(seconds_target=10.0):
 def streaming_read_ceiling(K, torch, elems_per_tensor=1 << 30, reps=5):
     """HBM streaming-read rate of committed code: the library's calibration
     scan (kv_calibrate_amax: contiguous fp16, 16-byte non-temporal loads, a
-    packed max per element) over two tensors of 2 GiB each. The call is
+    packed max per element) over two tensors of `elems_per_tensor` fp16 values
+    each (2 GiB each by default). The call is
     synchronous (it reads its status back), so HIP events bracket its kernels,
     the few-byte readback and the host's return; the same call on a 64 Ki-element
     input measures that fixed part, which is subtracted. Fastest of `reps`."""
@@ -538,8 +539,41 @@ def streaming_read_ceiling(K, torch, elems_per_tensor=1 << 30, reps=5):
     torch.cuda.empty_cache()
     return {"gbs": nbytes / (t_big - t_small) / 1e9, "bytes": nbytes, "call_us": t_big * 1e6,
             "fixed_us": t_small * 1e6,
-            "method": "kv_calibrate_amax over 2 x 2 GiB fp16 (HIP events, minus the same call on 2 x 64 Ki "
-                      "elements), fastest of %d" % reps}
+            "method": "kv_calibrate_amax over 2 x %d fp16 (HIP events, minus the same call on 2 x 64 Ki "
+                      "elements), fastest of %d" % (elems_per_tensor, reps)}
+
+
+def same_size_streaming_read(K, torch, nbytes, nsets=6, reps=12):
+    """The calibration scan (as in streaming_read_ceiling) over `nbytes` of fp16
+    split into two tensors, rotated over `nsets` separate copies so that, like
+    the attention points, no call finds its bytes in the caches (6 x 134 MB
+    exceeds the 256 MB Infinity Cache). Fixed part subtracted as above;
+    fastest call."""
+    n = nbytes // 4
+    bufs = [torch.ones((2, n), dtype=torch.float16, device="cuda") for _ in range(nsets)]
+    small = torch.ones((2, 1 << 16), dtype=torch.float16, device="cuda")
+    amax = torch.empty(2, dtype=torch.float32, device="cuda")
+    scale = torch.empty(2, dtype=torch.float32, device="cuda")
+
+    def timed(x):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        K.kv_calibrate_amax(x, amax, scale)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    for b in bufs:
+        timed(b)  # warm-up, and evicts the first copies before the timed calls
+    t_big = min(timed(bufs[i % nsets]) for i in range(reps))
+    t_small = min(timed(small) for _ in range(5))
+    del bufs
+    torch.cuda.empty_cache()
+    nb = 4 * n
+    return {"gbs": nb / (t_big - t_small) / 1e9, "bytes": nb, "call_us": t_big * 1e6, "fixed_us": t_small * 1e6,
+            "method": f"kv_calibrate_amax over 2 x {n} fp16 rotated over {nsets} copies (HIP events, minus the "
+                      f"same call on 2 x 64 Ki elements), fastest of {reps}"}
 
 
 COPY_BYTES = 1 << 30
@@ -773,6 +807,9 @@ def main():
     log("measuring the streaming-read ceiling")
     ceiling = streaming_read_ceiling(K, torch)
     log(f"streaming-read ceiling: {json.dumps(ceiling)}")
+    # the same scan over the 4k decode's K/V bytes: what a plain read of that size reaches, start-up included
+    same = same_size_streaming_read(K, torch, main["kv_bytes_per_step"])
+    log(f"same-size streaming read: {json.dumps(same)}")
     tps = {}
     for p, key in (("4k", "4k"), ("32k", "32k_derived_decode_b32"), ("256k", "256k")):
         if p in results:
@@ -808,7 +845,10 @@ def main():
                      "kernel": main["attn_kernel"], "kernel_us": main["attn_kernel_us"],
                      "measured_streaming_read_gbs": ceiling["gbs"],
                      "frac_of_measured_streaming_read": achieved / ceiling["gbs"],
-                     "streaming_read": ceiling},
+                     "streaming_read": ceiling,
+                     "same_size_streaming_read_gbs": same["gbs"],
+                     "frac_of_same_size_streaming_read": achieved / same["gbs"],
+                     "same_size_streaming_read": same},
         "cpu_baseline": cpu,
         "points": results,
     }
