@@ -585,7 +585,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
     // registers (reading it from LDS would make the compiler wait for the
     // staged loads, which it cannot tell apart from Q).
     static_assert(W * kTileBytes<D> <= (int)sizeof(sm_o), "tile staging must fit in the merge area");
-    uint8_t* tb = reinterpret_cast<uint8_t*>(&sm_o[0][0][0]) + wave * kTileBytes<D>;
+    uint8_t* tb = reinterpret_cast<uint8_t*>(&sm_o[0][0][0]) + __builtin_amdgcn_readfirstlane(wave) * kTileBytes<D>;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
