@@ -24,9 +24,9 @@ __device__ __forceinline__ u16x2 mag_max(u16x2 m, uint32_t w) {
 // grid (chunks, n_tensors), 256 threads; each block scans a contiguous chunk
 // of its tensor. vec8: rows are 16-byte aligned (n_elems % 8 == 0). The vector
 // path keeps eight 16-byte loads in flight per thread and takes the maximum of
-// two magnitudes per packed 16-bit instruction.
+// two magnitudes per packed 16-bit instruction. read_first: see the end.
 __global__ __launch_bounds__(256) void calib_amax(const uint16_t* __restrict__ x, int64_t n_elems,
-                                                  int64_t chunk, int vec8, uint32_t* acc) {
+                                                  int64_t chunk, int vec8, int read_first, uint32_t* acc) {
   constexpr int kUnroll = 8;
   const int64_t t = blockIdx.y;
   const uint16_t* row = x + t * n_elems;
@@ -57,15 +57,22 @@ __global__ __launch_bounds__(256) void calib_amax(const uint16_t* __restrict__ x
     for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) m = max(m, (uint32_t)(row[i] & 0x7FFFu));
   }
   // wave reduction, then the block's four wavefronts meet in LDS and one
-  // atomic per block folds the result in (the atomics of one tensor all go to
-  // one address and are served one after another)
+  // atomic per block folds the result in. The atomics of one tensor all go to
+  // one address and are served one after another; with many blocks per tensor
+  // (read_first) a block first reads the value folded in so far and skips its
+  // atomic when it has nothing larger. Any value it reads was held by acc
+  // during this launch (the clear kernel's zero or a later maximum), and acc
+  // only grows, so a skip never loses the maximum; an old value costs at most
+  // an unneeded atomic. With few blocks per tensor the read's round trip at
+  // the end of every block costs more than the atomics it saves.
   __shared__ uint32_t wmax[4];
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t b = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    if (b != 0u) atomicMax(acc + t, b);
+    if (read_first ? b > __hip_atomic_load(acc + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : b != 0u)
+      atomicMax(acc + t, b);
   }
 }
 
@@ -109,10 +116,14 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t n_tensors, int64_t n_elem
   }
   if (chunks < 1) chunks = 1;
   int vec8 = ((n_elems % 8) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  // Read before the atomic from 64 blocks per tensor up (134 MB in two tensors,
+  // 382 blocks each: 27.9 -> 23.7 us; 4 GiB: 672 -> 636 us; the same bytes in
+  // 48 tensors of 16 blocks: 24.4 us without the read, 31.0 with it).
+  const int read_first = chunks >= 64;
   for (int64_t t0 = 0; t0 < n_tensors; t0 += 65535) {
     int64_t nt = n_tensors - t0 < 65535 ? n_tensors - t0 : 65535;
     calib_amax<<<dim3((unsigned)chunks, (unsigned)nt), dim3(256), 0, stream>>>(
-        x + t0 * n_elems, n_elems, chunk, vec8, acc + t0);
+        x + t0 * n_elems, n_elems, chunk, vec8, read_first, acc + t0);
   }
   calib_finalize<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(amax, scale, n_tensors);
   return hipGetLastError();

@@ -102,6 +102,35 @@ def test_calibrate_error_statuses(K):
     assert amax.cpu().numpy()[1] == 0 and scale.cpu().numpy()[1] == 0
 
 
+@pytest.mark.parametrize("pattern", ["rising", "one_outlier", "negative_extremes", "late_nonfinite"])
+def test_calibrate_many_blocks(K, pattern):
+    """Two 8 Mi-element tensors (hundreds of scan blocks each). A block skips
+    its atomic when the maximum folded in so far is not below its own, so the
+    patterns put the maximum where every block, one block or the last block
+    has to fold it in, and a second call on other data must not see the first."""
+    n = 1 << 23
+    rng = np.random.default_rng({"rising": 11, "one_outlier": 12, "negative_extremes": 13, "late_nonfinite": 14}[pattern])
+    x = rng.standard_normal((2, n)).astype(np.float16)
+    if pattern == "rising":
+        x = (np.linspace(0.0, 300.0, n, dtype=np.float32)[None, :] * np.array([[1.0], [-0.5]], np.float32)).astype(np.float16)
+    elif pattern == "one_outlier":
+        x[0, int(rng.integers(n))] = 97.5
+        x[1, n - 1] = -311.0
+    elif pattern == "negative_extremes":
+        x[0, 5] = -65504.0
+        x[1, n // 2 + 3] = -60000.0
+        x[1, n // 2 + 4] = 59968.0
+    else:
+        x[0, n - 2] = np.inf
+        x[1, n - 7] = np.nan
+    for inp in (x, x[:, : n // 4].copy() * np.float16(0.5)):
+        amax, scale, st = K.kv_calibrate_amax(dev(inp), check=False)
+        ra, rs, rst = calibrate_amax(inp)
+        assert st == rst
+        assert np.array_equal(amax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), (amax, ra)
+        assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
 # ----------------------------------------------------------------- write
 
 def _gpu_write(K, db, ks, vs):
