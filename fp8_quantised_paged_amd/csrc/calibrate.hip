@@ -22,40 +22,45 @@ __device__ __forceinline__ u16x2 mag_max(u16x2 m, uint32_t w) {
 }
 
 // grid (chunks, n_tensors), 256 threads; each block scans a contiguous chunk
-// of its tensor. vec8: rows are 16-byte aligned (n_elems % 8 == 0). The vector
-// path keeps eight 16-byte loads in flight per thread and takes the maximum of
-// two magnitudes per packed 16-bit instruction. read_first: see the end.
+// [lo, hi) of its tensor. The 16-byte aligned middle of the chunk goes through
+// the vector loop, which keeps eight 16-byte loads in flight per thread and
+// takes the maximum of two magnitudes per packed 16-bit instruction; the at
+// most 7 elements before and after it (rows whose length is not a multiple of
+// 8 start at any even address) are read one per thread. read_first: see the end.
 __global__ __launch_bounds__(256) void calib_amax(const uint16_t* __restrict__ x, int64_t n_elems,
-                                                  int64_t chunk, int vec8, int read_first, uint32_t* acc) {
+                                                  int64_t chunk, int read_first, uint32_t* acc) {
   constexpr int kUnroll = 8;
   const int64_t t = blockIdx.y;
   const uint16_t* row = x + t * n_elems;
-  int64_t lo = (int64_t)blockIdx.x * chunk;
-  int64_t hi = lo + chunk < n_elems ? lo + chunk : n_elems;
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < n_elems ? lo + chunk : n_elems;
+  // elements up to the first 16-byte boundary at or after row + lo
+  int64_t head = (int64_t)((16u - ((unsigned)reinterpret_cast<uintptr_t>(row + lo) & 15u)) & 15u) / 2;
+  head = head < hi - lo ? head : hi - lo;
+  const int64_t vlo = lo + head;
+  const int64_t nvec = (hi - vlo) / 8;
+  const int64_t vhi = vlo + 8 * nvec;
   uint32_t m = 0u;
-  if (vec8) {
-    const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-    const int64_t end = hi / 8;
-    int64_t i = lo / 8 + threadIdx.x;
-    u16x2 m2 = {0, 0};
-    for (; i + (kUnroll - 1) * 256 < end; i += kUnroll * 256) {
-      u32x4 w[kUnroll];
+  if (threadIdx.x < head) m = row[lo + threadIdx.x] & 0x7FFFu;
+  if (threadIdx.x < hi - vhi) m = max(m, (uint32_t)(row[vhi + threadIdx.x] & 0x7FFFu));
+  const u32x4* rv = reinterpret_cast<const u32x4*>(row + vlo);
+  int64_t i = threadIdx.x;
+  u16x2 m2 = {0, 0};
+  for (; i + (kUnroll - 1) * 256 < nvec; i += kUnroll * 256) {
+    u32x4 w[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(rv + i + u * 256);
+    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(rv + i + u * 256);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m2 = mag_max(m2, w[u][j]);
-    }
-    for (; i < end; i += 256) {
-      const u32x4 w = __builtin_nontemporal_load(rv + i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m2 = mag_max(m2, w[j]);
-    }
-    m = max((uint32_t)m2[0], (uint32_t)m2[1]);
-  } else {
-    for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) m = max(m, (uint32_t)(row[i] & 0x7FFFu));
+      for (int j = 0; j < 4; ++j) m2 = mag_max(m2, w[u][j]);
   }
+  for (; i < nvec; i += 256) {
+    const u32x4 w = __builtin_nontemporal_load(rv + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m2 = mag_max(m2, w[j]);
+  }
+  m = max(m, max((uint32_t)m2[0], (uint32_t)m2[1]));
   // wave reduction, then the block's four wavefronts meet in LDS and one
   // atomic per block folds the result in. The atomics of one tensor all go to
   // one address and are served one after another; with many blocks per tensor
@@ -115,7 +120,6 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t n_tensors, int64_t n_elem
     chunks = (n_elems + chunk - 1) / chunk;
   }
   if (chunks < 1) chunks = 1;
-  int vec8 = ((n_elems % 8) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
   // Read before the atomic from 64 blocks per tensor up (134 MB in two tensors,
   // 382 blocks each: 27.9 -> 23.7 us; 4 GiB: 672 -> 636 us; the same bytes in
   // 48 tensors of 16 blocks: 24.4 us without the read, 31.0 with it).
@@ -123,7 +127,7 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t n_tensors, int64_t n_elem
   for (int64_t t0 = 0; t0 < n_tensors; t0 += 65535) {
     int64_t nt = n_tensors - t0 < 65535 ? n_tensors - t0 : 65535;
     calib_amax<<<dim3((unsigned)chunks, (unsigned)nt), dim3(256), 0, stream>>>(
-        x + t0 * n_elems, n_elems, chunk, vec8, read_first, acc + t0);
+        x + t0 * n_elems, n_elems, chunk, read_first, acc + t0);
   }
   calib_finalize<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(amax, scale, n_tensors);
   return hipGetLastError();

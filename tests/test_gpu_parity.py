@@ -131,6 +131,26 @@ def test_calibrate_many_blocks(K, pattern):
         assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
 
 
+def test_calibrate_odd_length_rows(K):
+    """Rows of 3,000,001 elements start at every even byte offset modulo 16,
+    so each scan block reads a few elements before and after its 16-byte
+    aligned middle one by one; the maxima sit in those pieces: a row's first
+    element, a row's last, and just past a block's start."""
+    n = 3_000_001
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((5, n)).astype(np.float16)
+    x[1, 0] = 200.0
+    x[2, n - 1] = -300.0
+    x[3, 20480 * 7 + 3] = 250.0
+    x[4, n // 2] = -6.0e4
+    for inp in (x, x[:4, : n - 6].copy()):
+        amax, scale, st = K.kv_calibrate_amax(dev(inp), check=False)
+        ra, rs, rst = calibrate_amax(inp)
+        assert st == rst == 0
+        assert np.array_equal(amax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), (amax, ra)
+        assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
 # ----------------------------------------------------------------- write
 
 def _gpu_write(K, db, ks, vs):
