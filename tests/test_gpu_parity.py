@@ -151,6 +151,22 @@ def test_calibrate_odd_length_rows(K):
         assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
 
 
+def test_calibrate_more_tensors_than_one_grid_row(K):
+    """70,000 tensors of 13 elements: the scan is launched in groups of at
+    most 65,535 tensors (the grid's y limit), and a row holds at most one
+    aligned 16-byte vector, the rest being read one element per thread. The
+    maxima sit in the second group, at its last tensor and at row ends."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((70_000, 13)).astype(np.float16)
+    x[65_535, 12] = 123.0
+    x[69_999, 0] = -456.0
+    amax, scale, st = K.kv_calibrate_amax(dev(x), check=False)
+    ra, rs, rst = calibrate_amax(x)
+    assert st == rst == 0
+    assert np.array_equal(amax.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
 # ----------------------------------------------------------------- write
 
 def _gpu_write(K, db, ks, vs):
