@@ -5,6 +5,35 @@
 namespace kvfp8 {
 namespace {
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// E4M3 codes of two fp32 values that are not NaN, written into the low
+// (HI = false) or high half of `old` (the other half is kept): the same codes
+// as e4m3_encode, with the clamp to +-448 as one median instruction and one
+// convert for the pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                                  __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), (int)old, HI);
+}
+
+// The fp32 quotient x / scale, correctly rounded, for an fp32 x and a normal
+// fp32 scale, as one fp64 multiply by rcp = 1 / scale rounded to fp64
+// (computed once on the host) and one rounding to fp32, instead of an fp32
+// division (about ten instructions, one of them a reciprocal). Why the result
+// is the same: write x = X 2^a with |X| < 2^24 and scale = S 2^c with
+// 2^23 <= S < 2^24. An fp32 rounding midpoint next to x / scale (in the fp32
+// normal range) is m = M 2^k with M odd and 2^24 <= M < 2^25; x = m scale
+// would need M to divide X, so x - m scale is a non-zero multiple of 2^(k+c),
+// and |x / scale - m| >= |m| / (M S) > 2^-49 |m|. The fp64 product is within
+// about 2^-52 of x / scale (two roundings to 53 bits), so no midpoint lies
+// between the two and both round to the same fp32 value. Zero, Inf and NaN
+// pass through; quotients below the fp32 normal range encode to a signed zero
+// either way.
+__device__ __forceinline__ float div_by_scale(float x, double rcp) {
+  return (float)((double)x * rcp);
+}
+
 // Calls with at most this many tokens use the one-thread-per-8-dims kernel.
 constexpr int64_t kDirectMaxTokens = 256;
 
@@ -15,7 +44,7 @@ constexpr int64_t kDirectMaxTokens = 256;
 __global__ __launch_bounds__(256) void quant_write_direct_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ slots, int64_t n_tokens, int n_kv_heads, int head_dim,
-    int page_size, int64_t num_pages, float k_scale, float v_scale, uint8_t* __restrict__ k_cache,
+    int page_size, int64_t num_pages, double k_rcp, double v_rcp, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache) {
   const int groups = head_dim >> 3;
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -38,7 +67,7 @@ __global__ __launch_bounds__(256) void quant_write_direct_kernel(
   for (int j = 0; j < 8; ++j) {
     uint32_t bits = (kw[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
     float x = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-    kc[j >> 2] |= e4m3_encode(x / k_scale) << ((j & 3) * 8);
+    kc[j >> 2] |= e4m3_encode(div_by_scale(x, k_rcp)) << ((j & 3) * 8);
   }
   uint8_t* kdst = k_cache + ((page * n_kv_heads + h) * page_size + off) * head_dim + g * 8;
   *reinterpret_cast<u32x2*>(kdst) = u32x2{kc[0], kc[1]};
@@ -48,7 +77,7 @@ __global__ __launch_bounds__(256) void quant_write_direct_kernel(
   for (int j = 0; j < 8; ++j) {
     uint32_t bits = (vw[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
     float x = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-    vdst[(int64_t)j * page_size] = (uint8_t)e4m3_encode(x / v_scale);
+    vdst[(int64_t)j * page_size] = (uint8_t)e4m3_encode(div_by_scale(x, v_rcp));
   }
 }
 
@@ -78,7 +107,7 @@ template <int D, int TPT>
 __global__ __launch_bounds__(8192 / (8 * TPT)) void quant_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ slots, int64_t n_tokens, int n_kv_heads, int page_shift,
-    int64_t num_pages, float k_scale, float v_scale, uint8_t* __restrict__ k_cache,
+    int64_t num_pages, double k_rcp, double v_rcp, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache) {
   constexpr int TB = 8192 / D;              // tokens per block: 64 or 128
   constexpr int NT = 8192 / (8 * TPT);      // threads per block
@@ -128,23 +157,66 @@ __global__ __launch_bounds__(8192 / (8 * TPT)) void quant_write_kernel(
       vw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + src));
     }
   }
-  uint32_t vword[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  // Encode. Without NaN inputs (the rule) two codes come from each convert,
+  // written into the chosen half of their word, after a one-instruction clamp
+  // to +-448; a NaN must keep its sign as 0x7F | sign, which the convert does
+  // not do, so a thread with any NaN input takes the per-value encoder. A NaN
+  // fp16 input is one whose magnitude bits exceed 0x7C00.
+  u16x2 mag = {0, 0};
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    uint32_t kc[2] = {0u, 0u};
+  for (int i = 0; i < TPT; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, kw[i][w] & 0x7FFF7FFFu));
+      mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, vw[i][w] & 0x7FFF7FFFu));
+    }
+  const bool nan_in = (mag[0] > 0x7C00u) || (mag[1] > 0x7C00u);
+  auto kq = [&](int i, int j) {  // fp32 quotient of K value (token i, dim 8g + j)
+    return div_by_scale((float)__builtin_bit_cast(_Float16, (uint16_t)(kw[i][j >> 1] >> ((j & 1) * 16))), k_rcp);
+  };
+  auto vq = [&](int i, int j) {
+    return div_by_scale((float)__builtin_bit_cast(_Float16, (uint16_t)(vw[i][j >> 1] >> ((j & 1) * 16))), v_rcp);
+  };
+  uint32_t kc[TPT][2];
+  uint32_t vword[8];
+  if (!nan_in) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t lo = e4m3_pack2<false>(kq(i, 4 * h2), kq(i, 4 * h2 + 1), 0u);
+        kc[i][h2] = e4m3_pack2<true>(kq(i, 4 * h2 + 2), kq(i, 4 * h2 + 3), lo);
+      }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t kb = (kw[i][j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-      const uint32_t vb = (vw[i][j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-      kc[j >> 2] |= e4m3_encode((float)__builtin_bit_cast(_Float16, (uint16_t)kb) / k_scale) << ((j & 3) * 8);
-      vword[j] |= e4m3_encode((float)__builtin_bit_cast(_Float16, (uint16_t)vb) / v_scale) << (i * 8);
+      if constexpr (TPT == 1) {
+        vword[j] = e4m3_pack2<false>(vq(0, j), 0.0f, 0u);
+      } else {
+        vword[j] = e4m3_pack2<false>(vq(0, j), vq(1, j), 0u);
+        if constexpr (TPT == 4) vword[j] = e4m3_pack2<true>(vq(2, j), vq(3, j), vword[j]);
+      }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vword[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      kc[i][0] = kc[i][1] = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kc[i][j >> 2] |= e4m3_encode(kq(i, j)) << ((j & 3) * 8);
+        vword[j] |= e4m3_encode(vq(i, j)) << (i * 8);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
     const int64_t s = sl[i];
     if (s >= 0 && s < cap) {
       const int64_t page = s >> page_shift;
       const int off = (int)(s & (page_size - 1));
       uint8_t* kdst = k_cache + ((page * n_kv_heads + h) * page_size + off) * D + 8 * g;
-      *reinterpret_cast<u32x2*>(kdst) = u32x2{kc[0], kc[1]};
+      *reinterpret_cast<u32x2*>(kdst) = u32x2{kc[i][0], kc[i][1]};
     }
   }
   uint8_t* vrow = reinterpret_cast<uint8_t*>(vbuf) + TPT * q;
@@ -265,10 +337,13 @@ hipError_t launch_quant_write(const uint16_t* k, const uint16_t* v, const int64_
                               int32_t page_size, int64_t num_pages, float k_scale, float v_scale,
                               uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
+  // reciprocals of the scales rounded to fp64, for div_by_scale
+  const double k_rcp = 1.0 / (double)k_scale;
+  const double v_rcp = 1.0 / (double)v_scale;
   if (n_tokens <= kDirectMaxTokens) {
     const int64_t total = n_tokens * n_kv_heads * (head_dim / 8);
     quant_write_direct_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-        k, v, slots, n_tokens, n_kv_heads, head_dim, page_size, num_pages, k_scale, v_scale, k_cache,
+        k, v, slots, n_tokens, n_kv_heads, head_dim, page_size, num_pages, k_rcp, v_rcp, k_cache,
         v_cache);
     return hipGetLastError();
   }
@@ -281,7 +356,7 @@ hipError_t launch_quant_write(const uint16_t* k, const uint16_t* v, const int64_
   // four workgroups per CU, then 512-thread ones (two tokens per thread)
   const bool wide = blocks * n_kv_heads < 4 * (int64_t)device_cus();
 #define QW_LAUNCH(DD, TT) quant_write_kernel<DD, TT><<<grid, dim3(8192 / (8 * TT)), 0, stream>>>( \
-      k, v, slots, n_tokens, n_kv_heads, shift, num_pages, k_scale, v_scale, k_cache, v_cache)
+      k, v, slots, n_tokens, n_kv_heads, shift, num_pages, k_rcp, v_rcp, k_cache, v_cache)
   if (head_dim == 128) {
     if (wide) QW_LAUNCH(128, 1); else QW_LAUNCH(128, 2);
   } else {

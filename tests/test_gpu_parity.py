@@ -266,6 +266,32 @@ def test_quant_write_skips_padding_and_saturates(K):
     assert (kc == 0x7E).any()
 
 
+@pytest.mark.parametrize("n_tok,hkv,D", [(600, 2, 128), (600, 2, 64), (70_000, 1, 128), (131_072, 1, 64)])
+def test_quant_write_grouped_nonfinite_and_extremes(K, n_tok, hkv, D):
+    """Calls of more than 256 tokens take the grouped write, which encodes two
+    codes per convert unless a thread holds a NaN input; NaN of both signs,
+    +-Inf, +-65504, -0 and fp16 subnormals are scattered over the call so
+    that wavefronts mix both paths. The small sizes run one token per
+    thread, the large ones (a grid of at least 1,024 workgroups) two."""
+    bt = make_batch([n_tok], [1], 4 * hkv, hkv, D, 16, seed=4700 + n_tok + D)
+    rng = np.random.default_rng(n_tok + D)
+    specials = np.array([np.nan, -np.nan, np.inf, -np.inf, 65504.0, -65504.0, -0.0, 6e-8, -6e-8, 2.0 ** -24],
+                        dtype=np.float16)
+    specials[1] = np.frombuffer(np.uint16(0xFE00).tobytes(), np.float16)[0]  # a NaN with the sign bit set
+    for arr in (bt.k, bt.v):
+        flat = arr.reshape(-1)
+        pos = rng.choice(flat.size, size=min(flat.size // 50, 4000), replace=False)
+        flat[pos] = specials[rng.integers(0, specials.size, pos.size)]
+    db = DeviceBatch(bt)
+    K.kv_quant_write(db.k, db.v, db.slots, 0.0123, 0.0456, db.k_cache, db.v_cache)
+    from oracle import new_caches, quant_write
+    kc, vc = new_caches(bt.num_pages, bt.n_kv_heads, bt.page_size, bt.head_dim)
+    quant_write(bt.k, bt.v, bt.slot_mapping, np.float32(0.0123), np.float32(0.0456), kc, vc)
+    assert np.array_equal(db.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy(), vc)
+    assert (kc == 0x7F).any() and (kc == 0xFF).any() and (vc == 0x7E).any() and (vc == 0xFE).any()
+
+
 # ----------------------------------------------------------------- attention
 
 def _run_decode(K, db, ks, vs, sm, S):
