@@ -429,32 +429,96 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
 
   // ---- append: each of the sequence's new tokens (key positions L - T ..
   // L - 1, this step's query tokens) is quantised into its slot, exactly as
-  // the cache write does, by the wavefront that will load the tile holding it,
-  // which then waits for its stores before any load of its own; no other
-  // wavefront or workgroup reads that tile (tiles and splits start on
-  // multiples of 64 keys, and pages hold at most 64).
+  // the cache write does, by the wavefront that will load the tile holding it;
+  // no other wavefront or workgroup reads that tile (tiles and splits start on
+  // multiples of 64 keys, and pages hold at most 64), and the wavefront's other
+  // tiles lie on other pages. Its stores must be complete before it issues the
+  // load of that tile (see below for where each pipeline waits).
+  constexpr bool kStaged = NB == 2 && P >= 16;
+  bool first_wait = false;
   if (a.k_new != nullptr && ntiles > 0) {
     const int first_new = max(start, L - T);
     if (first_new < end) {
       constexpr int PER = D / 64;  // dims per lane
       bool wrote = false;
-      for (int pos = first_new; pos < end; ++pos) {
-        if (wave != ((pos - start) / kTile) % W) continue;
-        const uint64_t page = (uint32_t)a.block_table[(int64_t)b * a.max_pages + pos / P];
-        const int off = pos % P;
-        const int64_t src = ((int64_t)(q0 + pos - (L - T)) * a.n_kv_heads + kvh) * D + PER * lane;
-        uint8_t* kd = a.k_cache_w + ((page * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
-        uint8_t* vd = a.v_cache_w + ((page * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
+      int wrote_tile = -1;
+      bool one_tile = true;
+      if constexpr (kStaged) {
+        // Staged verify (several new tokens): up to four tokens at a time, every
+        // load first (block-table entries and new values), then the encodes and
+        // stores; the wait counter retires loads and stores in issue order, so a
+        // token's loads placed after the previous token's stores would cost a
+        // memory round trip per token.
+        constexpr int kBatch = 4;
+        for (int p0 = first_new; p0 < end; p0 += kBatch) {
+          bool mine[kBatch];
+          bool any = false;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const float kx = (float)__builtin_bit_cast(_Float16, a.k_new[src + j]);
-          const float vx = (float)__builtin_bit_cast(_Float16, a.v_new[src + j]);
-          kd[j] = (uint8_t)e4m3_encode(kx / a.k_scale);
-          vd[(int64_t)j * P] = (uint8_t)e4m3_encode(vx / a.v_scale);
+          for (int u = 0; u < kBatch; ++u) {
+            mine[u] = p0 + u < end && wave == ((p0 + u - start) / kTile) % W;
+            any = any || mine[u];
+          }
+          if (!any) continue;
+          // unconditional loads (positions clamped to the split's new tokens):
+          // loads on one side of a branch would make the compiler wait for each
+          uint64_t page[kBatch];
+          uint16_t kx[kBatch][PER], vx[kBatch][PER];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int pos = min(p0 + u, end - 1);
+            page[u] = (uint32_t)a.block_table[(int64_t)b * a.max_pages + pos / P];
+            const int64_t src = ((int64_t)(q0 + pos - (L - T)) * a.n_kv_heads + kvh) * D + PER * lane;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+              kx[u][j] = a.k_new[src + j];
+              vx[u][j] = a.v_new[src + j];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            if (!mine[u]) continue;
+            const int pos = p0 + u;
+            const int tile = (pos - start) / kTile;
+            one_tile = one_tile && (wrote_tile < 0 || wrote_tile == tile);
+            wrote_tile = tile;
+            const int off = pos % P;
+            uint8_t* kd = a.k_cache_w + ((page[u] * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
+            uint8_t* vd = a.v_cache_w + ((page[u] * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+              kd[j] = (uint8_t)e4m3_encode((float)__builtin_bit_cast(_Float16, kx[u][j]) / a.k_scale);
+              vd[(int64_t)j * P] = (uint8_t)e4m3_encode((float)__builtin_bit_cast(_Float16, vx[u][j]) / a.v_scale);
+            }
+            wrote = true;
+          }
         }
-        wrote = true;
+      } else {
+        for (int pos = first_new; pos < end; ++pos) {
+          if (wave != ((pos - start) / kTile) % W) continue;
+          const uint64_t page = (uint32_t)a.block_table[(int64_t)b * a.max_pages + pos / P];
+          const int off = pos % P;
+          const int64_t src = ((int64_t)(q0 + pos - (L - T)) * a.n_kv_heads + kvh) * D + PER * lane;
+          uint8_t* kd = a.k_cache_w + ((page * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
+          uint8_t* vd = a.v_cache_w + ((page * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const float kx = (float)__builtin_bit_cast(_Float16, a.k_new[src + j]);
+            const float vx = (float)__builtin_bit_cast(_Float16, a.v_new[src + j]);
+            kd[j] = (uint8_t)e4m3_encode(kx / a.k_scale);
+            vd[(int64_t)j * P] = (uint8_t)e4m3_encode(vx / a.v_scale);
+          }
+          wrote = true;
+        }
       }
-      if (wrote) __builtin_amdgcn_s_waitcnt(0);
+      if (wrote) {
+        // The staged pipeline issues every tile load but its first behind a
+        // full wait, so it waits only when the tile is its first one; the
+        // register pipelines wait here (deferring it measured slower there).
+        if (kStaged && one_tile)
+          first_wait = wrote_tile == wave;
+        else
+          __builtin_amdgcn_s_waitcnt(0);
+      }
     }
   }
 
@@ -534,7 +598,6 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   // them), and the barrier waits for LDS only, so they stay in flight
   // across it (a full __syncthreads would also wait for every vector load).
   // the verify pipeline stages every tile, the first included, through LDS
-  constexpr bool kStaged = NB == 2 && P >= 16;
   __asm__ volatile("" ::: "memory");
   if (!kStaged && it < ntiles) {
     load_tile<D, P>(ra, pa, lo, kbase, vbase, page_stride);
@@ -591,6 +654,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
 #pragma unroll
       for (int c = 0; c < NC; ++c) __asm__ volatile("" ::"v"(qraw[nb][c]));  // Q complete before the loop
     if (it < ntiles) {
+      if (first_wait) __builtin_amdgcn_s_waitcnt(0);  // this step's new tokens are in this tile
       load_tile_lds<D, P>(tb, pa, lo, kbase, vbase, page_stride);
       __builtin_amdgcn_s_waitcnt(0);
       read_tile_lds<D, P>(ra, tb, lane);
