@@ -435,11 +435,36 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
   // tiles lie on other pages. Its stores must be complete before it issues the
   // load of that tile (see below for where each pipeline waits).
   constexpr bool kStaged = NB == 2 && P >= 16;
+  constexpr int PER = D / 64;  // dims per lane
+  constexpr int kBatch = 4;
   bool first_wait = false;
+  // Staged verify: a wavefront whose new tokens are one batch in one tile that
+  // is not its first issues their loads here and encodes and stores them once
+  // its first tile has landed (deferred), so the loads' round trip overlaps
+  // that tile's instead of delaying it.
+  bool deferred = false;
+  int d_p0 = 0, d_tile = -1;
+  bool d_mine[kBatch];
+  uint64_t d_page[kBatch];
+  uint16_t d_kx[kBatch][PER], d_vx[kBatch][PER];
+  auto store_batch = [&](int p0, const bool (&mine)[kBatch], const uint64_t (&page)[kBatch],
+                         const uint16_t (&kx)[kBatch][PER], const uint16_t (&vx)[kBatch][PER]) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (!mine[u]) continue;
+      const int off = (p0 + u) % P;
+      uint8_t* kd = a.k_cache_w + ((page[u] * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
+      uint8_t* vd = a.v_cache_w + ((page[u] * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        kd[j] = (uint8_t)e4m3_encode((float)__builtin_bit_cast(_Float16, kx[u][j]) / a.k_scale);
+        vd[(int64_t)j * P] = (uint8_t)e4m3_encode((float)__builtin_bit_cast(_Float16, vx[u][j]) / a.v_scale);
+      }
+    }
+  };
   if (a.k_new != nullptr && ntiles > 0) {
     const int first_new = max(start, L - T);
     if (first_new < end) {
-      constexpr int PER = D / 64;  // dims per lane
       bool wrote = false;
       int wrote_tile = -1;
       bool one_tile = true;
@@ -449,7 +474,6 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
         // stores; the wait counter retires loads and stores in issue order, so a
         // token's loads placed after the previous token's stores would cost a
         // memory round trip per token.
-        constexpr int kBatch = 4;
         for (int p0 = first_new; p0 < end; p0 += kBatch) {
           bool mine[kBatch];
           bool any = false;
@@ -474,23 +498,35 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
               vx[u][j] = a.v_new[src + j];
             }
           }
+          int btile = -1;
+          bool bone = true;
 #pragma unroll
           for (int u = 0; u < kBatch; ++u) {
             if (!mine[u]) continue;
-            const int pos = p0 + u;
-            const int tile = (pos - start) / kTile;
-            one_tile = one_tile && (wrote_tile < 0 || wrote_tile == tile);
-            wrote_tile = tile;
-            const int off = pos % P;
-            uint8_t* kd = a.k_cache_w + ((page[u] * a.n_kv_heads + kvh) * P + off) * D + PER * lane;
-            uint8_t* vd = a.v_cache_w + ((page[u] * a.n_kv_heads + kvh) * D + PER * lane) * P + off;
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-              kd[j] = (uint8_t)e4m3_encode((float)__builtin_bit_cast(_Float16, kx[u][j]) / a.k_scale);
-              vd[(int64_t)j * P] = (uint8_t)e4m3_encode((float)__builtin_bit_cast(_Float16, vx[u][j]) / a.v_scale);
-            }
-            wrote = true;
+            const int tile = (p0 + u - start) / kTile;
+            bone = bone && (btile < 0 || btile == tile);
+            btile = tile;
           }
+          if (end - first_new <= kBatch && bone && btile != wave) {
+            deferred = true;
+            d_p0 = p0;
+            d_tile = btile;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              d_mine[u] = mine[u];
+              d_page[u] = page[u];
+#pragma unroll
+              for (int j = 0; j < PER; ++j) {
+                d_kx[u][j] = kx[u][j];
+                d_vx[u][j] = vx[u][j];
+              }
+            }
+            continue;
+          }
+          store_batch(p0, mine, page, kx, vx);
+          one_tile = one_tile && bone && (wrote_tile < 0 || wrote_tile == btile);
+          wrote_tile = btile;
+          wrote = true;
         }
       } else {
         for (int pos = first_new; pos < end; ++pos) {
@@ -657,6 +693,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_split_kernel(const AttnArgs a)
       if (first_wait) __builtin_amdgcn_s_waitcnt(0);  // this step's new tokens are in this tile
       load_tile_lds<D, P>(tb, pa, lo, kbase, vbase, page_stride);
       __builtin_amdgcn_s_waitcnt(0);
+      if (deferred) {
+        store_batch(d_p0, d_mine, d_page, d_kx, d_vx);
+        if (d_tile == it + W) __builtin_amdgcn_s_waitcnt(0);  // the next load reads them
+      }
       read_tile_lds<D, P>(ra, tb, lane);
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (it + W < ntiles) load_tile_lds<D, P>(tb, pb, lo, kbase, vbase, page_stride);
