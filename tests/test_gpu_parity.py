@@ -393,6 +393,10 @@ VERIFY_APPEND_CASES = {
     "g4_p64": lambda: make_batch([700, 64, 129], [4, 2, 3], 16, 4, 128, 64, seed=83),
     # 32 rows per kv-head with pages of 4 (register tiles, no staging)
     "g8_p4_d64": lambda: make_batch([100, 257], [4, 2], 32, 4, 64, 4, seed=84),
+    # staged tiles of 32-key pages: at S = 1 the new tokens of the 700-key sequence lie in a wavefront's
+    # third tile and those of the 450-key one straddle two wavefronts' second tiles (both stored after
+    # the wavefront's first tile has landed)
+    "deferred_g8_p32": lambda: make_batch([700, 450, 40], [4, 4, 2], 32, 4, 128, 32, seed=85),
 }
 
 
