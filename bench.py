@@ -190,11 +190,17 @@ class Point:
         return g
 
     def time_steps(self, steps, warmup, fused=False):
-        """Exactly `steps` graph-replayed steps; returns (seconds per step, out)."""
+        """Exactly `steps` graph-replayed steps; returns (seconds per step, out).
+        The steps are captured as whole rotations of the cache copies, up to
+        STEPS_PER_GRAPH steps in one graph (as a captured multi-layer decode
+        would run them); the rest run as one-rotation graphs and, for a last
+        partial rotation, single-step graphs."""
         torch = self.torch
         n = len(self.sets)
         fn = self.step_fused if fused else self.step
-        full = self.capture(fn, n)
+        per_graph = n * max(1, min(steps // n, STEPS_PER_GRAPH // n))
+        full = self.capture(fn, per_graph)
+        rotation = self.capture(fn, n) if per_graph > n else full
         singles = [self.capture(lambda i, j=j: fn(j), 1) for j in range(n)]
         for w in range(warmup):
             singles[w % n].replay()
@@ -208,8 +214,11 @@ class Point:
         t0 = time.perf_counter()
         e0.record()
         done = 0
-        while done + n <= steps:
+        while done + per_graph <= steps:
             full.replay()
+            done += per_graph
+        while done + n <= steps:
+            rotation.replay()
             done += n
         while done < steps:
             singles[done % n].replay()
@@ -585,6 +594,8 @@ def same_size_scan(K, torch, nbytes, nsets=6, reps=12):
 
 
 COPY_BYTES = 1 << 30
+# steps captured in one graph by Point.time_steps (whole rotations of the cache copies)
+STEPS_PER_GRAPH = 60
 
 
 def counter_pass(K, torch, make_config, point="4k"):
@@ -629,7 +640,7 @@ def counter_pass(K, torch, make_config, point="4k"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--points", default="4k,32k,256k,mtp3,mixed,4k_p4,4k_tp4,4k_f16,mtp3_f16")
     ap.add_argument("--splits", type=int, default=0, help="splits of the 4k point (0: heuristic)")
