@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
 # FETCH_SIZE / WRITE_SIZE runs (`bench.py --counter-pass`), scaled by the same
 # counters' reading of a 1 GiB device copy. Valid only for the kernel source
 # they were taken on (sha256 prefix); otherwise the traffic is reported as null.
-MEASURED_TRAFFIC = {"source_sha256_prefix": "e5036034eda46ad7", "read_bytes": 136832583,
+MEASURED_TRAFFIC = {"source_sha256_prefix": "58c927dbd5d8d8ee", "read_bytes": 137039137,
                     "write_bytes": 1081344}
 
 

@@ -43,15 +43,22 @@ struct TileRegs {
 };
 
 __device__ __forceinline__ float wave_max_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  // lanes l and l ^ 16 meet by a swap of neighbouring 16-lane rows, then lanes
+  // l and l ^ 32 by a swap of the two halves (gfx950 cross-row moves on the
+  // vector ALU: no LDS round trip, no wait)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  // the same two swaps as the maximum; every lane of a group adds the same
+  // two values in the same order, so the group agrees bit for bit
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 
@@ -69,15 +76,18 @@ struct PageRegs {
 
 // Vector loads, issued two tiles ahead of use: the in-order vector memory
 // counter then never makes a wait on these ids wait on K/V bytes that are
-// still in flight for the tile being computed.
+// still in flight for the tile being computed. Key positions are never
+// negative, so the page index is an unsigned (shift) division.
 template <int P>
 __device__ __forceinline__ void load_pages(PageRegs<P>& pr, const int32_t* __restrict__ btrow, int t0,
                                            int last, int n, int g) {
   const int krel = 16 * (n >> 2) + (n & 3);
 #pragma unroll
-  for (int t = 0; t < PageRegs<P>::NK; ++t) pr.k[t] = btrow[min((t0 + krel + 4 * t) / P, last)];
+  for (int t = 0; t < PageRegs<P>::NK; ++t)
+    pr.k[t] = btrow[min((int)((uint32_t)(t0 + krel + 4 * t) / P), last)];
 #pragma unroll
-  for (int pc = 0; pc < PageRegs<P>::NV; ++pc) pr.v[pc] = btrow[min((t0 + 16 * g + pc * P) / P, last)];
+  for (int pc = 0; pc < PageRegs<P>::NV; ++pc)
+    pr.v[pc] = btrow[min((int)((uint32_t)(t0 + 16 * g + pc * P) / P), last)];
 }
 
 // Page ids of one 64-key tile (pages of >= 16 keys) taken from a block-table
@@ -99,8 +109,8 @@ __device__ __forceinline__ void pages_from_row(PageRegs<P>& pr, const int32_t (&
                                                int g) {
   static_assert(P >= 16, "one page id per lane for K and for V");
   const int krel = 16 * (n >> 2) + (n & 3);
-  pr.k[0] = row_entry(rowv, min((t0 + krel) / P, last));
-  pr.v[0] = row_entry(rowv, min((t0 + 16 * g) / P, last));
+  pr.k[0] = row_entry(rowv, min((int)((uint32_t)(t0 + krel) / P), last));
+  pr.v[0] = row_entry(rowv, min((int)((uint32_t)(t0 + 16 * g) / P), last));
 }
 
 // K/V bytes are read exactly once per call, so they are loaded non-temporally

@@ -27,15 +27,22 @@ constexpr int kTileF = 32;
 constexpr float kLazyF = 8.0f;  // lazy rescale threshold (log2 units), as in the E4M3 kernel
 
 __device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  // lanes l and l ^ 16 meet by a swap of neighbouring 16-lane rows, then lanes
+  // l and l ^ 32 by a swap of the two halves (gfx950 cross-row moves on the
+  // vector ALU: no LDS round trip, no wait)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  // the same two swaps as the maximum; every lane of a group adds the same
+  // two values in the same order, so the group agrees bit for bit
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int D>
@@ -55,9 +62,9 @@ template <int P>
 __device__ __forceinline__ void pages_f16(PagesF16& pg, const int32_t* __restrict__ btrow, int t0, int last, int n,
                                           int g) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) pg.k[t] = btrow[min((t0 + 8 * (n >> 2) + 4 * t + (n & 3)) / P, last)];
-  pg.v[0] = btrow[min((t0 + 8 * g) / P, last)];
-  pg.v[1] = P == 4 ? btrow[min((t0 + 8 * g + 4) / P, last)] : pg.v[0];
+  for (int t = 0; t < 2; ++t) pg.k[t] = btrow[min((int)((uint32_t)(t0 + 8 * (n >> 2) + 4 * t + (n & 3)) / P), last)];
+  pg.v[0] = btrow[min((int)((uint32_t)(t0 + 8 * g) / P), last)];
+  pg.v[1] = P == 4 ? btrow[min((int)((uint32_t)(t0 + 8 * g + 4) / P), last)] : pg.v[0];
 }
 
 // Loads are unconditional: keys past the end of the sequence read the clamped
